@@ -1,0 +1,253 @@
+/*
+ * pkv.h -- C ABI of libpkv, the paged-KV attention hot path for AMD MI355X
+ * (gfx950, CDNA4).
+ *
+ * The pages this follows (cited by title and section):
+ *  [NV1] "nano-vLLM-1" (senjlearning.space): "3. KV cache 分配" (the per-layer
+ *        cache view [num_blocks, block_size, kv_heads, head_dim]),
+ *        "4. prefill 输入打包" (prepare_block_tables, prepare_prefill),
+ *        "5. deocde 输入打包" (prepare_decode and why prefill needs block
+ *        tables only on a prefix hit), BlockManager "3. 核心方法一：分配"
+ *        (the slot of position p is block_table[p / bs] * bs + p % bs).
+ *  [MR]  "Nano vLLM 解读（5）：解析 ModelRunner" (languisher.top):
+ *        "FlashAttention Kernel 函参准备" (the three groups of kernel inputs),
+ *        "prepare_prefill" / "prepare_decode" (cu_seqlens, slot_mapping,
+ *        block_tables, context_lens), and the ModelRunner init (attention
+ *        writes new K/V through slot_mapping and reads history through
+ *        block_tables).
+ *  [ES]  "【nano-vllm 学习】04 - 自顶向下的引擎调度层源码学习2" (kyonqi.github.io):
+ *        "KV-Cache … 是什么？" (softmax(QK^T / sqrt(d_k)) V with a causal mask)
+ *        and "PageAttention" (blocks as pages, block_table as page table).
+ *
+ * Conventions for every device entry point:
+ *  - All device pointers are caller-owned and must stay valid until the stream
+ *    reaches the call. The library keeps no device state between calls, never
+ *    synchronises, and allocates no device memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Tensors are row-major; strides are in ELEMENTS. The caches are the
+ *    per-layer views [num_blocks, block_size, num_kv_heads, head_dim],
+ *    contiguous.
+ *  - Every call validates its host-side arguments and returns a pkv_status;
+ *    on failure nothing is launched and pkv_last_error() describes why.
+ *    Device-resident metadata (slots, block tables, lengths) is not read on
+ *    the host. A slot outside [0, num_blocks*block_size) is skipped by the
+ *    store; a block-table entry outside [0, num_blocks), or a length beyond
+ *    what the table covers, makes the affected output rows unspecified but
+ *    never causes an access outside the caches.
+ *  - Thread-safe across host threads and streams; calls that overlap on one
+ *    stream are ordered by it.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_EINVAL = 1,        /* an argument is outside its documented range     */
+    PKV_EUNSUPPORTED = 2,  /* valid, but no kernel for this dtype/shape        */
+    PKV_ELAUNCH = 3,       /* the HIP runtime reported an error on launch      */
+    PKV_ENOSPACE = 4       /* a caller-provided buffer is too small            */
+} pkv_status;
+
+typedef enum {
+    PKV_F32 = 0,           /* IEEE binary32                                     */
+    PKV_BF16 = 1           /* bfloat16; accumulation is fp32                    */
+} pkv_dtype;
+
+/* PKV_ABI_VERSION of the loaded library. */
+int pkv_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling host thread.
+ * The pointer stays valid until the next call on that thread. */
+const char *pkv_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * store_kvcache  ([MR] ModelRunner init and "prepare_prefill": slot_mapping
+ * says where each new token's K/V is written; [NV1] "3. KV cache 分配" fixes
+ * the cache view.)
+ *
+ * For i in [0, num_tokens): s = slot_mapping[i]; if 0 <= s < num_blocks *
+ * block_size, copy k row i ([num_kv_heads, head_dim] elements) bit for bit to
+ * k_cache viewed as [num_blocks * block_size, num_kv_heads, head_dim] row s,
+ * and likewise v -> v_cache. Negative slots (padding) are skipped.
+ *
+ *  k, v            [num_tokens, num_kv_heads, head_dim] with token strides
+ *                  k_token_stride / v_token_stride (elements; the rows of one
+ *                  token are contiguous). May be slices of a fused QKV buffer.
+ *  k_cache,v_cache [num_blocks, block_size, num_kv_heads, head_dim].
+ *  slot_mapping    device int32 [num_tokens]. Slots must be unique within a
+ *                  call (each token owns its slot); duplicates leave the row
+ *                  with one of the written values.
+ *  dtype           PKV_F32 or PKV_BF16 (a bit copy: dtype only sizes rows).
+ * Requires head_dim * num_kv_heads * element_size and the token strides to be
+ * multiples of 16 bytes and all pointers 16-byte aligned. num_tokens == 0 is a
+ * no-op. */
+int pkv_store_kvcache(const void *k, const void *v, int64_t k_token_stride,
+                      int64_t v_token_stride, void *k_cache, void *v_cache,
+                      const int32_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                      int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * prefill_attention_varlen  ([MR] "FlashAttention Kernel 函参准备" and
+ * "prepare_prefill"; [NV1] "5. deocde 输入打包", block tables on a prefix hit;
+ * [ES] the attention equation and causal mask.)
+ *
+ * Sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) and keys
+ * [0, Lk_s) with Lk_s = cu_seqlens_k[s+1] - cu_seqlens_k[s] >= Lq_s. Query i
+ * of sequence s sits at position Lk_s - Lq_s + i and attends to keys 0..that
+ * position (bottom-right causal alignment; the diagonal is visible). For each
+ * q head h, kv head h / (num_q_heads / num_kv_heads):
+ *     out[row, h, :] = softmax(scale * q[row, h, :] . K^T) V
+ *
+ * Keys and values come from
+ *  - block_tables == NULL: the call's contiguous k, v rows
+ *    [cu_seqlens_k[s] + j] ([total_k, num_kv_heads, head_dim], token stride
+ *    kv_token_stride). Requires Lk_s == Lq_s (no cached prefix).
+ *  - block_tables != NULL: the caches, position j of sequence s at slot
+ *    block_tables[s * max_blocks_per_seq + j / block_size] * block_size +
+ *    j % block_size. The K/V of this call's tokens must already have been
+ *    stored (pkv_store_kvcache on the same stream, before this call).
+ *
+ *  q               [total_q, num_q_heads, head_dim], token stride q_token_stride.
+ *  out             [total_q, num_q_heads, head_dim], contiguous, q's dtype.
+ *  cu_seqlens_q/_k device int32 [num_seqs + 1], prefix sums starting at 0.
+ *  max_seqlen_q/_k host upper bounds of Lq_s / Lk_s (size the launch grid).
+ *  dtype           PKV_BF16 (MFMA path for head_dim 128) or PKV_F32.
+ * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128},
+ * block_size a power of two in [1, 1024] when block_tables != NULL. */
+int pkv_prefill_attention_varlen(const void *q, int64_t q_token_stride, const void *k,
+                                 const void *v, int64_t kv_token_stride, const void *k_cache,
+                                 const void *v_cache, const int32_t *block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q,
+                                 const int32_t *cu_seqlens_k, int32_t num_seqs,
+                                 int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, float scale,
+                                 int32_t dtype, void *out, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * decode_attention_paged  ([MR] "prepare_decode": one query per sequence,
+ * context_lens keys read through block_tables; split-context partitions and
+ * their log-sum-exp combine follow Flash-Decoding (Dao et al., 2023).)
+ *
+ * For each sequence b with n = context_lens[b] and q head h:
+ *     out[b, h, :] = softmax(scale * q[b, h, :] . K_b^T) V_b
+ * over positions 0..n-1, position j at slot
+ * block_tables[b * max_blocks_per_seq + j / block_size] * block_size +
+ * j % block_size. The token being decoded must already be stored (its K/V is
+ * position n-1). n == 0 (a padded row) gives an all-zero output row.
+ *
+ * The context is split into partitions of `partition_size` tokens (0 = the
+ * library's choice; otherwise a positive multiple of 16). A sequence with more than
+ * one partition writes per-partition partial results to `workspace`, and a
+ * second kernel combines them; the workspace must hold
+ * pkv_decode_workspace_bytes(...) bytes (256-byte aligned), and may be NULL
+ * when that is 0.
+ *
+ *  q               [num_seqs, num_q_heads, head_dim], token stride q_token_stride.
+ *  out             [num_seqs, num_q_heads, head_dim], contiguous, q's dtype.
+ *  block_tables    device int32 [num_seqs, max_blocks_per_seq], -1 padded.
+ *  context_lens    device int32 [num_seqs].
+ *  max_context_len host upper bound of context_lens (sizes the grid and the
+ *                  workspace).
+ * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128}, block_size
+ * a power of two in [1, 1024]. */
+int pkv_decode_attention_paged(const void *q, int64_t q_token_stride, const void *k_cache,
+                               const void *v_cache, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               int32_t num_seqs, int32_t max_context_len, int32_t num_blocks,
+                               int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, float scale, int32_t dtype, void *out,
+                               int32_t partition_size, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Partition size the decode call will use for these arguments (resolves 0). */
+int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t max_context_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t dtype,
+                                  int32_t partition_size);
+
+/* Workspace bytes pkv_decode_attention_paged needs for these arguments. */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t dtype,
+                                  int32_t partition_size);
+
+/* ---------------------------------------------------------------------------
+ * Host metadata packing ([NV1] "4. prefill 输入打包" and "5. deocde 输入打包":
+ * prepare_block_tables, prepare_prefill, prepare_decode; pinned memory and
+ * one asynchronous host-to-device copy.)
+ *
+ * A batch is described on the host by, per sequence s:
+ *   seq_lens[s]          len(seq): tokens including this step's,
+ *   num_cached_tokens[s] leading tokens whose K/V is already in the cache
+ *                        (prefill; decode uses seq_lens[s] - 1 implicitly),
+ *   block table          bt_ids[bt_offsets[s] .. bt_offsets[s+1]) (CSR).
+ *
+ * pkv_plan_* computes the layout of one packed buffer; pkv_pack_* fills a host
+ * buffer (ideally pinned) with it; pkv_upload copies it to the device with one
+ * hipMemcpyAsync. Each array starts at a 256-byte-aligned offset.
+ *
+ * Prefill packs, in this order:
+ *   slot_mapping   int32 [num_slots]   slots of positions
+ *                  [num_cached_tokens[s], seq_lens[s]) of each s, in order
+ *   cu_seqlens_q   int32 [num_seqs+1]  prefix sums of seq_lens - num_cached
+ *   cu_seqlens_k   int32 [num_seqs+1]  prefix sums of seq_lens
+ *   block_tables   int32 [num_seqs, max_blocks_per_seq], -1 padded, present
+ *                  only when the batch has a cached prefix (total_k > total_q)
+ * Decode packs:
+ *   slot_mapping   int32 [num_seqs]    slot of position seq_lens[s] - 1
+ *   context_lens   int32 [num_seqs]    seq_lens[s]
+ *   block_tables   int32 [num_seqs, max_blocks_per_seq], -1 padded (always)
+ * Errors: PKV_EINVAL if a sequence's table has fewer than ceil(len / bs)
+ * entries, a length is negative (prefill) or < 1 (decode), num_cached exceeds
+ * len, or a count overflows int32; PKV_ENOSPACE if the buffer is too small. */
+typedef struct {
+    int32_t num_seqs;
+    int32_t total_q;             /* query rows (prefill) or num_seqs (decode)  */
+    int64_t total_k;             /* sum of seq_lens                            */
+    int32_t max_seqlen_q;
+    int32_t max_seqlen_k;        /* also the decode max_context_len            */
+    int32_t max_blocks_per_seq;
+    int32_t has_block_tables;
+    int32_t num_slots;
+    int32_t is_prefill;
+    int64_t off_slot_mapping;    /* byte offsets into the packed buffer; -1 if */
+    int64_t off_cu_seqlens_q;    /* the array is absent                        */
+    int64_t off_cu_seqlens_k;
+    int64_t off_context_lens;
+    int64_t off_block_tables;
+    int64_t total_bytes;
+} pkv_batch_layout;
+
+int pkv_plan_prefill(int32_t num_seqs, const int32_t *seq_lens,
+                     const int32_t *num_cached_tokens, const int64_t *bt_offsets,
+                     int32_t block_size, pkv_batch_layout *layout);
+int pkv_pack_prefill(int32_t num_seqs, const int32_t *seq_lens,
+                     const int32_t *num_cached_tokens, const int32_t *bt_ids,
+                     const int64_t *bt_offsets, int32_t block_size,
+                     const pkv_batch_layout *layout, void *host_buf, size_t host_bytes);
+int pkv_plan_decode(int32_t num_seqs, const int32_t *seq_lens, const int64_t *bt_offsets,
+                    int32_t block_size, pkv_batch_layout *layout);
+int pkv_pack_decode(int32_t num_seqs, const int32_t *seq_lens, const int32_t *bt_ids,
+                    const int64_t *bt_offsets, int32_t block_size,
+                    const pkv_batch_layout *layout, void *host_buf, size_t host_bytes);
+
+/* One asynchronous host-to-device copy of `bytes` from host_buf (pinned for
+ * true asynchrony) to dev_buf on `stream`. */
+int pkv_upload(const void *host_buf, void *dev_buf, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -214,3 +214,20 @@ def run_workload(w, nthreads: int = 0):
 
 def max_threads() -> int:
     return int(lib().orc_max_threads())
+
+
+def pools_after_store(w):
+    """The pools after this step's writes (history, then the new tokens),
+    without attending: (k_pool, v_pool, new-token slots)."""
+    _, dt = as_storage(w.q[:0])
+    kp = new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, dt)
+    vp = new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, dt)
+    if w.hist:
+        hs = slots(w.hist, w.block_tables, w.block_size)
+        store(w.k_hist, kp, hs)
+        store(w.v_hist, vp, hs)
+    ns = slots([(s, c, n) for s, (n, c) in enumerate(zip(w.seq_lens, w.num_cached))],
+               w.block_tables, w.block_size)
+    store(w.k_new, kp, ns)
+    store(w.v_new, vp, ns)
+    return kp, vp, ns

@@ -1,0 +1,273 @@
+// api.hip -- the extern "C" entry points of libpkv (declared in include/pkv.h):
+// host-side validation, launch configuration and workspace layout. No device
+// memory is allocated and nothing synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int launched(hipError_t e, const char *what) {
+    if (e == hipErrorNotSupported)
+        return fail(PKV_EUNSUPPORTED, "%s: no kernel for this dtype/shape", what);
+    if (e != hipSuccess) return fail(PKV_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return PKV_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int64_t x) {
+    int r = 0;
+    while ((int64_t(1) << r) < x) ++r;
+    return r;
+}
+int elem_size(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+bool dtype_ok(int32_t dtype) { return dtype == PKV_F32 || dtype == PKV_BF16; }
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+// Workspace: [num_seqs][maxparts][Hq][d] fp32 accumulators, then
+// [num_seqs][maxparts][Hq][2] fp32 (max, sum), each 256-byte aligned.
+struct DecodeWs {
+    int32_t P, maxparts;
+    int64_t acc_bytes, ml_bytes, total;
+};
+
+int resolve_partition(int32_t num_seqs, int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t d,
+                      int32_t bs, int32_t dtype, int32_t requested) {
+    if (requested > 0) return requested;
+    const int32_t group = Hkv > 0 ? Hq / Hkv : 1;
+    return pkv::decode_auto_partition(num_seqs, max_ctx, Hkv, bs, dtype, d, group);
+}
+
+DecodeWs decode_ws(int32_t num_seqs, int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t d,
+                   int32_t bs, int32_t dtype, int32_t requested) {
+    DecodeWs w;
+    w.P = resolve_partition(num_seqs, max_ctx, Hq, Hkv, d, bs, dtype, requested);
+    w.maxparts = max_ctx > 0 ? (int32_t)((max_ctx + (int64_t)w.P - 1) / w.P) : 1;
+    if (w.maxparts <= 1) {
+        w.maxparts = 1;
+        w.acc_bytes = w.ml_bytes = w.total = 0;
+        return w;
+    }
+    w.acc_bytes = align256((int64_t)num_seqs * w.maxparts * Hq * d * 4);
+    w.ml_bytes = align256((int64_t)num_seqs * w.maxparts * Hq * 2 * 4);
+    w.total = w.acc_bytes + w.ml_bytes;
+    return w;
+}
+
+}  // namespace
+
+extern "C" int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+extern "C" const char *pkv_last_error(void) { return g_err; }
+
+extern "C" int pkv_store_kvcache(const void *k, const void *v, int64_t k_token_stride,
+                                 int64_t v_token_stride, void *k_cache, void *v_cache,
+                                 const int32_t *slot_mapping, int32_t num_tokens,
+                                 int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t dtype, void *stream) {
+    const char *fn = "pkv_store_kvcache";
+    if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
+    if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens < 0", fn);
+    if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PKV_EINVAL, "%s: non-positive shape", fn);
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    if (num_slots > INT32_MAX) return fail(PKV_EINVAL, "%s: pool has more than 2^31-1 slots", fn);
+    const int es = elem_size(dtype);
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if ((row * es) % 16) return fail(PKV_EUNSUPPORTED, "%s: row bytes not a multiple of 16", fn);
+    if (k_token_stride < row || v_token_stride < row)
+        return fail(PKV_EINVAL, "%s: token stride smaller than a row", fn);
+    if ((k_token_stride * es) % 16 || (v_token_stride * es) % 16)
+        return fail(PKV_EINVAL, "%s: token strides must be multiples of 16 bytes", fn);
+    if (num_tokens == 0) return PKV_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+        return fail(PKV_EINVAL, "%s: null pointer", fn);
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PKV_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    pkv::StoreArgs a;
+    a.k = (const uint8_t *)k;
+    a.v = (const uint8_t *)v;
+    a.k_stride_bytes = k_token_stride * es;
+    a.v_stride_bytes = v_token_stride * es;
+    a.kc = (uint8_t *)k_cache;
+    a.vc = (uint8_t *)v_cache;
+    a.slots = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.chunks_per_row = (int32_t)(row * es / 16);
+    a.num_slots = num_slots;
+    return launched(pkv::launch_store(a, (hipStream_t)stream), fn);
+}
+
+static int check_attention_shape(const char *fn, int32_t dtype, int32_t Hq, int32_t Hkv,
+                                 int32_t d, int32_t num_seqs) {
+    if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
+        return fail(PKV_EINVAL, "%s: num_q_heads must be a positive multiple of num_kv_heads", fn);
+    if (d != 64 && d != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim must be 64 or 128", fn);
+    if (num_seqs < 0 || num_seqs > 65535) return fail(PKV_EINVAL, "%s: num_seqs out of [0, 65535]", fn);
+    return PKV_OK;
+}
+
+static int check_pool(const char *fn, const void *kc, const void *vc, const int32_t *bt,
+                      int32_t maxb, int32_t num_blocks, int32_t bs) {
+    if (!kc || !vc || !bt) return fail(PKV_EINVAL, "%s: null cache or block table", fn);
+    if (!aligned16(kc) || !aligned16(vc)) return fail(PKV_EINVAL, "%s: caches must be 16-byte aligned", fn);
+    if (!is_pow2(bs) || bs > 1024) return fail(PKV_EINVAL, "%s: block_size must be a power of two <= 1024", fn);
+    if (num_blocks <= 0 || maxb <= 0) return fail(PKV_EINVAL, "%s: num_blocks and max_blocks_per_seq must be positive", fn);
+    if ((int64_t)num_blocks * bs > INT32_MAX) return fail(PKV_EINVAL, "%s: pool has more than 2^31-1 slots", fn);
+    return PKV_OK;
+}
+
+extern "C" int pkv_prefill_attention_varlen(
+    const void *q, int64_t q_token_stride, const void *k, const void *v, int64_t kv_token_stride,
+    const void *k_cache, const void *v_cache, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+    int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_blocks, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t dtype, void *out, void *stream) {
+    const char *fn = "pkv_prefill_attention_varlen";
+    int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs);
+    if (rc) return rc;
+    if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+        return fail(PKV_EINVAL, "%s: negative length", fn);
+    if (max_seqlen_q > max_seqlen_k && block_tables)
+        return fail(PKV_EINVAL, "%s: max_seqlen_q > max_seqlen_k", fn);
+    if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
+    if (!q || !out || !cu_seqlens_q || !cu_seqlens_k) return fail(PKV_EINVAL, "%s: null pointer", fn);
+    const int es = elem_size(dtype);
+    if (q_token_stride < (int64_t)num_q_heads * head_dim)
+        return fail(PKV_EINVAL, "%s: q token stride smaller than a row", fn);
+    if (!aligned16(q) || !aligned16(out) || (q_token_stride * es) % 16)
+        return fail(PKV_EINVAL, "%s: q/out must be 16-byte aligned with 16-byte strides", fn);
+    pkv::PrefillArgs a;
+    a.q = q;
+    a.q_stride = q_token_stride;
+    a.paged = block_tables != nullptr;
+    if (a.paged) {
+        rc = check_pool(fn, k_cache, v_cache, block_tables, max_blocks_per_seq, num_blocks, block_size);
+        if (rc) return rc;
+        a.k = a.v = nullptr;
+        a.kv_stride = 0;
+    } else {
+        if (!k || !v) return fail(PKV_EINVAL, "%s: null k/v without block tables", fn);
+        if (kv_token_stride < (int64_t)num_kv_heads * head_dim)
+            return fail(PKV_EINVAL, "%s: kv token stride smaller than a row", fn);
+        if (!aligned16(k) || !aligned16(v) || (kv_token_stride * es) % 16)
+            return fail(PKV_EINVAL, "%s: k/v must be 16-byte aligned with 16-byte strides", fn);
+        a.k = k;
+        a.v = v;
+        a.kv_stride = kv_token_stride;
+    }
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.bt = block_tables;
+    a.maxb = max_blocks_per_seq;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.num_seqs = num_seqs;
+    a.num_blocks = num_blocks;
+    a.bs = a.paged ? block_size : 1;
+    a.log2bs = ilog2(a.bs);
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.d = head_dim;
+    a.group = num_q_heads / num_kv_heads;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out = out;
+    a.max_seqlen_q = max_seqlen_q;
+    return launched(pkv::launch_prefill(a, dtype, (hipStream_t)stream), fn);
+}
+
+extern "C" int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t max_context_len,
+                                             int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t block_size, int32_t dtype,
+                                             int32_t partition_size) {
+    return resolve_partition(num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim,
+                             block_size, dtype, partition_size);
+}
+
+extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len,
+                                             int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t block_size, int32_t dtype,
+                                             int32_t partition_size) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+    return (size_t)decode_ws(num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim,
+                             block_size, dtype, partition_size).total;
+}
+
+extern "C" int pkv_decode_attention_paged(
+    const void *q, int64_t q_token_stride, const void *k_cache, const void *v_cache,
+    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+    int32_t num_seqs, int32_t max_context_len, int32_t num_blocks, int32_t block_size,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t dtype,
+    void *out, int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "pkv_decode_attention_paged";
+    int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs);
+    if (rc) return rc;
+    if (max_context_len < 0) return fail(PKV_EINVAL, "%s: negative max_context_len", fn);
+    if (partition_size < 0 || partition_size % 16)
+        return fail(PKV_EINVAL, "%s: partition_size must be 0 or a positive multiple of 16", fn);
+    if (num_seqs == 0) return PKV_OK;
+    if (!q || !out || !context_lens) return fail(PKV_EINVAL, "%s: null pointer", fn);
+    rc = check_pool(fn, k_cache, v_cache, block_tables, max_blocks_per_seq, num_blocks, block_size);
+    if (rc) return rc;
+    const int es = elem_size(dtype);
+    if (q_token_stride < (int64_t)num_q_heads * head_dim)
+        return fail(PKV_EINVAL, "%s: q token stride smaller than a row", fn);
+    if (!aligned16(q) || !aligned16(out) || (q_token_stride * es) % 16)
+        return fail(PKV_EINVAL, "%s: q/out must be 16-byte aligned with 16-byte strides", fn);
+    const DecodeWs ws = decode_ws(num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim,
+                                  block_size, dtype, partition_size);
+    if ((int64_t)workspace_bytes < ws.total)
+        return fail(PKV_ENOSPACE, "%s: workspace needs %lld bytes", fn, (long long)ws.total);
+    if (ws.total > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
+        return fail(PKV_EINVAL, "%s: workspace must be non-null and 256-byte aligned", fn);
+    pkv::DecodeArgs a;
+    a.q = q;
+    a.q_stride = q_token_stride;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.bt = block_tables;
+    a.maxb = max_blocks_per_seq;
+    a.ctx = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_blocks = num_blocks;
+    a.bs = block_size;
+    a.log2bs = ilog2(block_size);
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.d = head_dim;
+    a.group = num_q_heads / num_kv_heads;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out = out;
+    a.P = ws.P;
+    a.maxparts = ws.maxparts;
+    a.ws_acc = ws.total ? (float *)workspace : nullptr;
+    a.ws_ml = ws.total ? (float *)((char *)workspace + ws.acc_bytes) : nullptr;
+    return launched(pkv::launch_decode(a, dtype, (hipStream_t)stream), fn);
+}
+
+extern "C" int pkv_upload(const void *host_buf, void *dev_buf, size_t bytes, void *stream) {
+    if (bytes == 0) return PKV_OK;
+    if (!host_buf || !dev_buf) return fail(PKV_EINVAL, "pkv_upload: null pointer");
+    hipError_t e = hipMemcpyAsync(dev_buf, host_buf, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PKV_ELAUNCH, "pkv_upload: %s", hipGetErrorString(e));
+    return PKV_OK;
+}
+
+// Used by the packers (pack.cpp) to report errors through pkv_last_error.
+int pkv_internal_fail(int code, const char *msg) { return fail(code, "%s", msg); }

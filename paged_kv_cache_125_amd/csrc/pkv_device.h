@@ -1,0 +1,100 @@
+// pkv_device.h -- device helpers shared by the gfx950 kernels of libpkv.
+//
+// Written for CDNA4 only: 64-wide wavefronts, bf16 MFMA, DPP row operations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// A bf16 value is the upper half of an fp32: widening is a shift or a mask.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte global loads/stores through the vector memory path.
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// DPP lane exchange inside a 16-lane row (the controls are the CDNA DPP
+// encodings: quad_perm, row_half_mirror, row_mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Max / sum over the 16 lanes of a row; every lane of the row gets the result.
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp<kQuadSwap1>(x));
+    x = fmaxf(x, dpp<kQuadSwap2>(x));
+    x = fmaxf(x, dpp<kRowHalfMirror>(x));
+    x = fmaxf(x, dpp<kRowMirror>(x));
+    return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<kQuadSwap1>(x);
+    x += dpp<kQuadSwap2>(x);
+    x += dpp<kRowHalfMirror>(x);
+    x += dpp<kRowMirror>(x);
+    return x;
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) {
+    int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+__device__ __forceinline__ float shfl(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+// Max / sum over a whole wave (64 lanes).
+__device__ __forceinline__ float wave_max(float x) {
+    x = row16_max(x);
+    x = fmaxf(x, shfl_xor(x, 16));
+    x = fmaxf(x, shfl_xor(x, 32));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row16_sum(x);
+    x += shfl_xor(x, 16);
+    x += shfl_xor(x, 32);
+    return x;
+}
+
+// Compiler-level ordering point for LDS traffic exchanged between lanes of
+// one wave (DS instructions of a wave execute in order).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace pkv

@@ -1,0 +1,61 @@
+// pkv_internal.h -- launchers shared between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct StoreArgs {
+    const uint8_t *k, *v;
+    int64_t k_stride_bytes, v_stride_bytes;
+    uint8_t *kc, *vc;
+    const int32_t *slots;
+    int32_t num_tokens;
+    int32_t chunks_per_row;   // row bytes / 16
+    int64_t num_slots;
+};
+hipError_t launch_store(const StoreArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q;
+    int64_t q_stride;          // elements between consecutive sequences' q rows
+    const void *kc, *vc;
+    const int32_t *bt;
+    int32_t maxb;
+    const int32_t *ctx;
+    int32_t num_seqs, num_blocks, bs, log2bs;
+    int32_t Hq, Hkv, d, group;
+    float scale_log2;          // scale * log2(e): scores live in the exp2 domain
+    void *out;
+    int32_t P;                 // tokens per partition
+    int32_t maxparts;          // ceil(max_context_len / P)
+    float *ws_acc;             // [num_seqs][maxparts][Hq][d]
+    float *ws_ml;              // [num_seqs][maxparts][Hq][2]  (max, sum)
+};
+// Returns hipErrorNotSupported when no kernel covers the shape/dtype.
+hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t stream);
+int32_t decode_auto_partition(int32_t num_seqs, int32_t max_ctx, int32_t Hkv, int32_t bs,
+                              int dtype, int32_t d, int32_t group);
+bool decode_has_mfma_path(int dtype, int32_t d, int32_t group);
+
+struct PrefillArgs {
+    const void *q;
+    int64_t q_stride;
+    const void *k, *v;         // contiguous source (paged == 0)
+    int64_t kv_stride;
+    const void *kc, *vc;       // paged source (paged == 1)
+    const int32_t *bt;
+    int32_t maxb;
+    int32_t paged;
+    const int32_t *cu_q, *cu_k;
+    int32_t num_seqs, num_blocks, bs, log2bs;
+    int32_t Hq, Hkv, d, group;
+    float scale_log2;
+    void *out;
+    int32_t max_seqlen_q;
+};
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);
+
+}  // namespace pkv

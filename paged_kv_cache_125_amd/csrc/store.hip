@@ -1,0 +1,62 @@
+// store.hip -- store_kvcache: write each new token's K/V row into the pool
+// slot named by slot_mapping.
+//
+// ("Nano vLLM 解读（5）：解析 ModelRunner", ModelRunner init and
+//  "prepare_prefill": the attention layer writes new K/V via slot_mapping into
+//  the per-layer cache view [num_blocks, block_size, kv_heads, head_dim] of
+//  "nano-vLLM-1", "3. KV cache 分配".)
+//
+// A pure bit copy bound by HBM: every (token, 16-byte chunk) pair of the K row
+// and of the V row is one work item. Consecutive lanes take consecutive chunks
+// of one row, so each wave instruction moves whole 64-byte segments; every
+// thread keeps UNROLL items (2*UNROLL loads) in flight before its stores.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int kStoreThreads = 256;
+constexpr int kStoreUnroll = 4;
+
+__global__ __launch_bounds__(kStoreThreads) void store_kvcache_kernel(StoreArgs a) {
+    const int64_t total = (int64_t)a.num_tokens * a.chunks_per_row;
+    const int64_t base = (int64_t)blockIdx.x * (kStoreThreads * kStoreUnroll) + threadIdx.x;
+    const int64_t row_bytes = (int64_t)a.chunks_per_row * 16;
+    u32x4 kx[kStoreUnroll], vx[kStoreUnroll];
+    int64_t dst[kStoreUnroll];
+#pragma unroll
+    for (int u = 0; u < kStoreUnroll; ++u) {
+        const int64_t item = base + (int64_t)u * kStoreThreads;
+        dst[u] = -1;
+        if (item < total) {
+            const int32_t t = (int32_t)(item / a.chunks_per_row);
+            const int32_t c = (int32_t)(item - (int64_t)t * a.chunks_per_row);
+            const int32_t s = a.slots[t];
+            if (s >= 0 && s < a.num_slots) {
+                kx[u] = ld16(a.k + t * a.k_stride_bytes + c * 16);
+                vx[u] = ld16(a.v + t * a.v_stride_bytes + c * 16);
+                dst[u] = (int64_t)s * row_bytes + c * 16;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kStoreUnroll; ++u) {
+        if (dst[u] >= 0) {
+            st16(a.kc + dst[u], kx[u]);
+            st16(a.vc + dst[u], vx[u]);
+        }
+    }
+}
+
+hipError_t launch_store(const StoreArgs &a, hipStream_t stream) {
+    const int64_t total = (int64_t)a.num_tokens * a.chunks_per_row;
+    if (total == 0) return hipSuccess;
+    const int64_t per_block = (int64_t)kStoreThreads * kStoreUnroll;
+    const int64_t blocks = (total + per_block - 1) / per_block;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(store_kvcache_kernel, dim3((unsigned)blocks), dim3(kStoreThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

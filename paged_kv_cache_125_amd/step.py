@@ -1,0 +1,92 @@
+"""One pass of the hot path over a batch: pack the step's metadata on the host
+(one pinned buffer, one copy), store this step's K/V into the pool, then run
+prefill or decode attention. All compute is in libpkv's kernels.
+
+The batch is described the way the pages' ModelRunner sees it: per sequence,
+its length, how many leading tokens are already cached, and its block table.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from . import (decode_attention_paged, decode_workspace_bytes, pack_decode, pack_prefill,
+               prefill_attention_varlen, store_kvcache)
+
+
+def alloc_pool(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+               dtype: torch.dtype, device, fill: float = float("nan")) -> Tuple[torch.Tensor, torch.Tensor]:
+    """K and V caches [num_blocks, bs, Hkv, d], every element ``fill`` (NaN by
+    default, so a read of an unwritten slot shows in the output)."""
+    shape = (num_blocks, block_size, num_kv_heads, head_dim)
+    k = torch.full(shape, fill, dtype=dtype, device=device)
+    v = torch.full(shape, fill, dtype=dtype, device=device)
+    return k, v
+
+
+def write_ranges(ranges: Sequence[Tuple[int, int, int]], block_tables: Sequence[Sequence[int]],
+                 block_size: int, k_rows: torch.Tensor, v_rows: torch.Tensor,
+                 k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Store K/V rows for positions [b, e) of sequences s, for each (s, b, e),
+    rows in list order -- e.g. a cached prefix written before the step."""
+    if not ranges:
+        return
+    meta = pack_prefill([e for _, _, e in ranges], [b for _, b, _ in ranges],
+                        [block_tables[s] for s, _, _ in ranges], block_size,
+                        device=k_cache.device, stream=stream)
+    store_kvcache(k_rows, v_rows, k_cache, v_cache, meta["slot_mapping"], stream=stream)
+
+
+@dataclass
+class StepInputs:
+    phase: str
+    seq_lens: List[int]
+    num_cached: List[int]
+    block_tables: List[List[int]]
+    block_size: int
+    scale: float
+    use_block_tables: bool = True
+    partition_size: int = 0
+
+
+def run_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+             k_cache: torch.Tensor, v_cache: torch.Tensor, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Pack + store + attention for one step. Decode: one new token per
+    sequence (num_cached = len - 1). Prefill: keys read from the pool through
+    the block tables when the batch has a cached prefix (or when
+    ``use_block_tables``), else from this step's contiguous k/v."""
+    dev = k_cache.device
+    if s.phase == "decode":
+        meta = pack_decode(s.seq_lens, s.block_tables, s.block_size, device=dev, stream=stream)
+        store_kvcache(k_new, v_new, k_cache, v_cache, meta["slot_mapping"], stream=stream)
+        return decode_attention_paged(q, k_cache, v_cache, meta["block_tables"],
+                                      meta["context_lens"], meta["max_seqlen_k"], s.scale,
+                                      out=out, partition_size=s.partition_size,
+                                      workspace=workspace, stream=stream)
+    meta = pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size, device=dev,
+                        stream=stream)
+    store_kvcache(k_new, v_new, k_cache, v_cache, meta["slot_mapping"], stream=stream)
+    bt = meta["block_tables"]
+    if bt is None and s.use_block_tables:
+        # a batch without a cached prefix may still read its keys from the pool
+        meta_bt = pack_decode(s.seq_lens, s.block_tables, s.block_size, device=dev, stream=stream)
+        bt = meta_bt["block_tables"]
+    if bt is not None:
+        return prefill_attention_varlen(q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                        meta["max_seqlen_q"], meta["max_seqlen_k"], s.scale,
+                                        k_cache=k_cache, v_cache=v_cache, block_tables=bt,
+                                        out=out, stream=stream)
+    return prefill_attention_varlen(q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                    meta["max_seqlen_q"], meta["max_seqlen_k"], s.scale,
+                                    k=k_new, v=v_new, out=out, stream=stream)
+
+
+def step_inputs_of(w, partition_size: int = 0) -> StepInputs:
+    """StepInputs from any object with the batch fields (e.g. a seeded workload)."""
+    return StepInputs(phase=w.phase, seq_lens=list(w.seq_lens), num_cached=list(w.num_cached),
+                      block_tables=[list(t) for t in w.block_tables], block_size=w.block_size,
+                      scale=w.scale, use_block_tables=w.use_block_tables,
+                      partition_size=partition_size)
