@@ -1,0 +1,438 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of each of the metric's
+two workloads, inputs resident in HBM:
+
+  decode : pack metadata (host, one pinned buffer, one copy) -> store_kvcache
+           of the new token of each sequence -> paged decode attention with
+           split-context partitions and the combine. Workload: Qwen3-0.6B-
+           shaped decode (16 q / 8 kv heads, head_dim 128, block size 256,
+           64 sequences, context U{512..4096}).
+  prefill: pack -> store_kvcache of every prompt token -> varlen causal
+           prefill attention. Workload: 16 prompts U{128..2048} under a
+           16384-token budget, 16 q / 8 kv heads, head_dim 128.
+
+`value` is the decode attention's algorithmic HBM throughput (GB/s); the
+prefill attention's TFLOP/s is reported beside it. Each call is timed with HIP
+events on the stream it runs on. Several copies of the inputs are used in
+rotation so that no step finds its data in the 256 MB last-level cache.
+
+`--workload` selects other presets (each alone): decode-long (Qwen3-8B-shaped,
+512 sequences, log-uniform 256..32768) and prefill-prefix (32 x 2048 with a
+cached 1024-token prefix on half of them).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "paged decode attn HBM GB/s (% peak) + varlen prefill attn TFLOP/s (% MFMA peak)"
+
+WORKLOADS = {
+    "default": [("decode", 2), ("prefill", 3)],
+    "decode": [("decode", 2)],
+    "prefill": [("prefill", 3)],
+    "decode-long": [("decode", 5)],
+    "prefill-prefix": [("prefill", 4)],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- work counts
+
+def decode_bytes(w) -> float:
+    """Algorithmic bytes of one decode attention call: every context token's K
+    and V row of every kv head, q and out, the block-table entries in use and
+    the context lengths."""
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    ctx = np.asarray(w.seq_lens, dtype=np.int64)
+    kv = int(ctx.sum()) * 2 * w.num_kv_heads * w.head_dim * es
+    qo = 2 * len(ctx) * w.num_q_heads * w.head_dim * es
+    meta = int(np.sum(-(-ctx // w.block_size))) * 4 + len(ctx) * 4
+    return float(kv + qo + meta)
+
+
+def store_bytes(w) -> float:
+    """Read the new K and V rows, write them, read the slot: per token
+    2 * (2 * Hkv * d * es) + 4 bytes."""
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    return float(w.total_q * (2 * (2 * w.num_kv_heads * w.head_dim * es) + 4))
+
+
+def prefill_flops(w) -> float:
+    """4 * d * Hq per visible (query, key) pair, the diagonal included."""
+    pairs = 0
+    for n, c in zip(w.seq_lens, w.num_cached):
+        lq = n - c
+        pairs += lq * c + lq * (lq + 1) // 2
+    return float(4 * w.head_dim * w.num_q_heads * pairs)
+
+
+# ----------------------------------------------------------------- GPU side
+
+class Part:
+    """One workload of the step, with `ncopies` resident copies of its inputs."""
+
+    def __init__(self, phase, preset, ncopies):
+        import paged_kv_cache_125_amd as pkv
+        from paged_kv_cache_125_amd.step import alloc_pool, step_inputs_of, write_ranges
+        from workloads import make_workload
+        self.pkv = pkv
+        self.phase, self.preset = phase, preset
+        self.copies = []
+        w = None
+        for c in range(ncopies):
+            w = make_workload(preset, device="cuda")
+            kc, vc = alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype, "cuda")
+            write_ranges(w.hist, w.block_tables, w.block_size, w.k_hist, w.v_hist, kc, vc)
+            w.k_hist = w.v_hist = None      # only the pool holds the history now
+            out = torch.empty_like(w.q)
+            self.copies.append((w, kc, vc, out))
+        self.w = w
+        self.s = step_inputs_of(w)
+        if phase == "decode":
+            need = pkv.decode_workspace_bytes(len(w.seq_lens), max(w.seq_lens), w.num_q_heads,
+                                              w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+            self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+            self.partition = pkv.decode_partition_size(len(w.seq_lens), max(w.seq_lens),
+                                                       w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                                       w.block_size, w.dtype)
+        self.names = ["pack", "store", "attention"]
+        self.times = {n: [] for n in self.names}
+        torch.cuda.synchronize()
+
+    def run(self, i, events):
+        """One pass; events is a list of 4 torch.cuda.Event or None."""
+        pkv, s = self.pkv, self.s
+        w, kc, vc, out = self.copies[i % len(self.copies)]
+        rec = (lambda j: events[j].record()) if events else (lambda j: None)
+        rec(0)
+        if self.phase == "decode":
+            meta = pkv.pack_decode(s.seq_lens, s.block_tables, s.block_size)
+            rec(1)
+            pkv.store_kvcache(w.k_new, w.v_new, kc, vc, meta["slot_mapping"])
+            rec(2)
+            pkv.decode_attention_paged(w.q, kc, vc, meta["block_tables"], meta["context_lens"],
+                                       meta["max_seqlen_k"], s.scale, out=out, workspace=self.ws)
+            rec(3)
+        else:
+            meta = pkv.pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size)
+            rec(1)
+            pkv.store_kvcache(w.k_new, w.v_new, kc, vc, meta["slot_mapping"])
+            rec(2)
+            if meta["block_tables"] is not None:
+                pkv.prefill_attention_varlen(w.q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                             meta["max_seqlen_q"], meta["max_seqlen_k"], s.scale,
+                                             k_cache=kc, v_cache=vc,
+                                             block_tables=meta["block_tables"], out=out)
+            else:
+                pkv.prefill_attention_varlen(w.q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                             meta["max_seqlen_q"], meta["max_seqlen_k"], s.scale,
+                                             k=w.k_new, v=w.v_new, out=out)
+            rec(3)
+        return meta   # keeps the packed buffers alive until the stream has run
+
+    def collect(self, events_per_step):
+        for evs in events_per_step:
+            for j, n in enumerate(self.names):
+                self.times[n].append(evs[j].elapsed_time(evs[j + 1]) * 1e-3)
+
+    def summary(self):
+        w = self.w
+        t_attn = float(np.mean(self.times["attention"]))
+        t_store = float(np.mean(self.times["store"]))
+        t_pack = float(np.mean(self.times["pack"]))
+        sb = store_bytes(w)
+        d = {"workload": w.name, "preset": self.preset, "phase": self.phase,
+             "num_seqs": len(w.seq_lens), "tokens_q": w.total_q,
+             "context_tokens": int(sum(w.seq_lens)),
+             "pack_us": t_pack * 1e6, "store_us": t_store * 1e6, "attention_us": t_attn * 1e6,
+             "attention_us_p10": float(np.percentile(self.times["attention"], 10)) * 1e6,
+             "attention_us_p90": float(np.percentile(self.times["attention"], 90)) * 1e6,
+             "store_GBps": sb / t_store / 1e9, "store_frac_hbm": sb / t_store / 1e9 / HBM_PEAK_GBS}
+        if self.phase == "decode":
+            b = decode_bytes(w)
+            d.update({"attention_bytes": b, "attention_GBps": b / t_attn / 1e9,
+                      "attention_frac_hbm": b / t_attn / 1e9 / HBM_PEAK_GBS,
+                      "partition_size": self.partition})
+        else:
+            f = prefill_flops(w)
+            d.update({"attention_flops": f, "attention_TFLOPs": f / t_attn / 1e12,
+                      "attention_frac_mfma": f / t_attn / 1e12 / MFMA_BF16_PEAK_TFLOPS})
+        return d
+
+
+# ----------------------------------------------------------------- oracle side
+
+def cpu_baseline(phase, preset, budget_s):
+    """The oracle, as it stands, on the host cores: store + attention of the
+    preset (decode: every sequence; prefill: as many whole sequences as fit
+    the time budget), repeated while the budget allows. Returns the rate in the
+    unit of the GPU figure (GB/s for decode, TFLOP/s for prefill)."""
+    import oracle
+    from workloads import make_workload, restrict
+    shape = make_workload(preset, values=False)
+    threads = oracle.max_threads()
+    if phase == "decode":
+        # whole sequences from the front of the batch, up to ~200K context tokens
+        take, tot = [], 0
+        for s, n in enumerate(shape.seq_lens):
+            if take and tot + n > 200_000:
+                break
+            take.append(s)
+            tot += n
+        w = restrict(shape, take)
+        kp, vp, slots = oracle.pools_after_store(w)     # setup: history + first write
+        reps, t = 0, 0.0
+        while t < budget_s and reps < 50:
+            t0 = time.perf_counter()
+            oracle.store(w.k_new, kp, slots)
+            oracle.store(w.v_new, vp, slots)
+            oracle.attention(w.q, w.q_lens, w.seq_lens, w.num_kv_heads, w.scale,
+                             k_cache=kp, v_cache=vp, tables=w.block_tables, block_size=w.block_size)
+            t += time.perf_counter() - t0
+            reps += 1
+        rate = decode_bytes(w) * reps / t / 1e9
+        return {"value": rate, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": f"{len(take)} of {len(shape.seq_lens)} sequences ({tot} context tokens): "
+                          f"oracle store + decode attention, {reps} repetition(s), {t:.1f} s",
+                "cpu": platform.processor() or platform.machine()}
+    w = make_workload(preset)
+    # prefill: a prefix of the batch, whole sequences, within the budget
+    from copy import copy
+    order = list(range(len(w.seq_lens)))
+    t, done, flops = 0.0, 0, 0.0
+    qo = np.concatenate([[0], np.cumsum(w.q_lens)])
+    for s in order:
+        sub = copy(w)
+        sub.seq_lens, sub.num_cached = [w.seq_lens[s]], [w.num_cached[s]]
+        sub.block_tables = [w.block_tables[s]]
+        sub.q, sub.k_new, sub.v_new = w.q[qo[s]:qo[s + 1]], w.k_new[qo[s]:qo[s + 1]], w.v_new[qo[s]:qo[s + 1]]
+        if w.num_cached[s] > 0:
+            break   # prefix presets: keep the sample to uncached sequences
+        t0 = time.perf_counter()
+        oracle.attention(sub.q, sub.q_lens, sub.seq_lens, w.num_kv_heads, w.scale,
+                         k=sub.k_new, v=sub.v_new)
+        t += time.perf_counter() - t0
+        flops += prefill_flops(sub)
+        done += 1
+        if t >= budget_s:
+            break
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(w.seq_lens)} sequences of the preset, oracle prefill "
+                      f"attention, {t:.1f} s",
+            "cpu": platform.processor() or platform.machine()}
+
+
+# ----------------------------------------------------------------- traffic
+
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
+CALIBRATION_BYTES = 1 << 30     # the plain device copy timed under the counters
+
+
+def _source_sha(kernel_file: str) -> str:
+    src = os.path.join(ROOT, "paged_kv_cache_125_amd", "csrc", kernel_file)
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def counters_traffic(kernel_file: str, key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    the kernel source changed since they were taken."""
+    try:
+        ent = json.load(open(COUNTERS_JSON))[key]
+        if ent.get("source_sha") != _source_sha(kernel_file):
+            return None
+        return ent["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _read_counter_csvs(d):
+    """{kernel name: {counter: [value per dispatch]}} from a rocprofv3 --pmc run."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            out.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir, workload):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what they read for
+    the calibration copy of CALIBRATION_BYTES, and store HBM bytes per launch
+    of the hot kernels in profiles/counters.json."""
+    f, w = _read_counter_csvs(fetch_dir), _read_counter_csvs(write_dir)
+
+    def avg(tab, needle, counter):
+        vals = [v for k, c in tab.items() if needle in k for v in c.get(counter, [])]
+        return sum(vals) / len(vals) if vals else None
+
+    kib = CALIBRATION_BYTES / 1024
+
+    def calib(tab, counter):
+        # the 1 GiB copies, not the small metadata uploads that share the blit kernel
+        vals = [v for k, c in tab.items() if "copy" in k.lower() for v in c.get(counter, []) if v > kib / 2]
+        return sum(vals) / len(vals) if vals else None
+
+    copy_f, copy_w = calib(f, "FETCH_SIZE"), calib(w, "WRITE_SIZE")
+    if copy_f is None or copy_w is None:
+        raise SystemExit("no calibration copy kernel in the counter runs")
+    ff, fw = copy_f / kib, copy_w / kib
+    data = json.load(open(COUNTERS_JSON)) if os.path.exists(COUNTERS_JSON) else {}
+    groups = {
+        "decode": (["decode_blk_kernel", "decode_mfma_kernel", "decode_reduce_kernel"], "decode.hip"),
+        "prefill": (["prefill_mfma_kernel"], "prefill.hip"),
+        "store": (["store_kvcache_kernel"], "store.hip"),
+    }
+    presets = {p for _, p in WORKLOADS[workload]}
+    for name, (kernels, src) in groups.items():
+        fetch = sum(avg(f, k, "FETCH_SIZE") or 0.0 for k in kernels)
+        write = sum(avg(w, k, "WRITE_SIZE") or 0.0 for k in kernels)
+        if fetch == 0 and write == 0:
+            continue
+        for p in presets:
+            data[f"{name}-preset{p}"] = {
+                "kernels": kernels, "source_sha": _source_sha(src),
+                "fetch_kib_raw": fetch, "write_kib_raw": write,
+                "copy_calibration": {"bytes": CALIBRATION_BYTES, "fetch_factor": ff, "write_factor": fw},
+                "hbm_bytes_per_launch": (fetch / ff + write / fw) * 1024,
+                "note": "mean over dispatches; the store of a step mixes its two workloads"
+                        if name == "store" and len(presets) > 1 else "mean over dispatches"}
+    os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
+    json.dump(data, open(COUNTERS_JSON, "w"), indent=1, sort_keys=True)
+    print(json.dumps({k: data[k]["hbm_bytes_per_launch"] for k in sorted(data)}, indent=1))
+
+
+# ----------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="default", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work per part")
+    ap.add_argument("--copies", type=int, default=0, help="resident input copies (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy (scales the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs into profiles/counters.json and exit")
+    args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.workload)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no sharding, no collectives). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    import paged_kv_cache_125_amd as pkv
+    pkv.lib()
+
+    parts = []
+    for phase, preset in WORKLOADS[args.workload]:
+        nc = args.copies or (2 if (phase == "decode" and preset == 5) else 3)
+        log(f"[bench] setting up {phase} preset {preset} ({nc} copies)")
+        parts.append(Part(phase, preset, nc))
+
+    if args.copy_calibration:
+        src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    log("[bench] warmup")
+    for i in range(args.warmup):
+        metas = [p.run(i, None) for p in parts]
+    torch.cuda.synchronize()
+
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in parts]
+              for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    keep = []
+    for i in range(args.steps):
+        keep.append([p.run(i, events[i][j]) for j, p in enumerate(parts)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del keep
+    for j, p in enumerate(parts):
+        p.collect([events[i][j] for i in range(args.steps)])
+    summaries = [p.summary() for p in parts]
+    log("[bench] " + json.dumps(summaries))
+
+    cpu = {}
+    if not args.no_cpu_baseline:
+        for p in parts:
+            log(f"[bench] oracle cpu baseline: {p.phase} preset {p.preset}")
+            cpu[p.phase] = cpu_baseline(p.phase, p.preset, args.cpu_budget)
+
+    dec = next((s for s in summaries if s["phase"] == "decode"), None)
+    pre = next((s for s in summaries if s["phase"] == "prefill"), None)
+    if dec is not None:
+        value, unit = dec["attention_GBps"], "GB/s"
+        per_launch = dec["attention_bytes"]
+        roof = {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": value / HBM_PEAK_GBS,
+                "traffic": counters_traffic("decode.hip", f"decode-preset{dec['preset']}"),
+                "kernel": "decode_mfma_kernel + decode_reduce_kernel (one decode_attention_paged call)",
+                "algorithmic_bytes_per_launch": per_launch, "avg_launch_us": dec["attention_us"]}
+        cpu_main = cpu.get("decode")
+    else:
+        value, unit = pre["attention_TFLOPs"], "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": value, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": value / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": counters_traffic("prefill.hip", f"prefill-preset{pre['preset']}"),
+                "kernel": "prefill_mfma_kernel", "algorithmic_flops_per_launch": pre["attention_flops"],
+                "avg_launch_us": pre["attention_us"]}
+        cpu_main = cpu.get("prefill")
+    names = {2: "decode-qwen3-0.6b-b64-ctx512-4096", 3: "prefill-varlen-16x-u128-2048-budget16384",
+             4: "prefill-prefix-hit-32x2048", 5: "decode-qwen3-8b-b512-ctx256-32768"}
+    config = {"workload": " + ".join(names[p.preset] for p in parts),
+              "parts": [{"phase": p.phase, **p.w.describe()} for p in parts],
+              "copies_in_rotation": [len(p.copies) for p in parts]}
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": config, "roofline": roof, "cpu_baseline": cpu_main,
+        "secondary": {}, "parts": summaries, "cpu_baselines": cpu,
+    }
+    if pre is not None:
+        line["secondary"]["prefill_attention_TFLOPs"] = pre["attention_TFLOPs"]
+        line["secondary"]["prefill_frac_of_mfma_peak"] = pre["attention_frac_mfma"]
+    if dec is not None:
+        line["secondary"]["decode_frac_of_hbm_peak"] = dec["attention_frac_hbm"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

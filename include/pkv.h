@@ -122,8 +122,9 @@ int pkv_store_kvcache(const void *k, const void *v, int64_t k_token_stride,
  *  cu_seqlens_q/_k device int32 [num_seqs + 1], prefix sums starting at 0.
  *  max_seqlen_q/_k host upper bounds of Lq_s / Lk_s (size the launch grid).
  *  dtype           PKV_BF16 (MFMA path for head_dim 128) or PKV_F32.
- * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128},
- * block_size a power of two in [1, 1024] when block_tables != NULL. */
+ * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128}, a
+ * positive finite scale, and block_size a power of two in [1, 1024] when
+ * block_tables != NULL. */
 int pkv_prefill_attention_varlen(const void *q, int64_t q_token_stride, const void *k,
                                  const void *v, int64_t kv_token_stride, const void *k_cache,
                                  const void *v_cache, const int32_t *block_tables,
@@ -146,12 +147,17 @@ int pkv_prefill_attention_varlen(const void *q, int64_t q_token_stride, const vo
  * j % block_size. The token being decoded must already be stored (its K/V is
  * position n-1). n == 0 (a padded row) gives an all-zero output row.
  *
- * The context is split into partitions of `partition_size` tokens (0 = the
- * library's choice; otherwise a positive multiple of 16). A sequence with more than
- * one partition writes per-partition partial results to `workspace`, and a
- * second kernel combines them; the workspace must hold
+ * Contexts are split so that every part of the GPU gets work, and the parts
+ * are combined by a second kernel. With partition_size == 0 the library
+ * chooses: for bf16, head_dim 128 and a block_size that is a multiple of 64
+ * (nano-vLLM's 256 included) the (sequence, kv head, 64-position chunk) work
+ * list is divided evenly over all waves the GPU holds at once, each wave
+ * finishing the sequences it covers entirely and leaving at most two partial
+ * results; otherwise fixed partitions are used. A positive multiple of 16
+ * forces fixed partitions of that many positions. The workspace must hold
  * pkv_decode_workspace_bytes(...) bytes (256-byte aligned), and may be NULL
- * when that is 0.
+ * when that is 0. pkv_decode_partition_size() reports the fixed partition
+ * size, or 0 for the balanced split.
  *
  *  q               [num_seqs, num_q_heads, head_dim], token stride q_token_stride.
  *  out             [num_seqs, num_q_heads, head_dim], contiguous, q's dtype.
@@ -159,8 +165,8 @@ int pkv_prefill_attention_varlen(const void *q, int64_t q_token_stride, const vo
  *  context_lens    device int32 [num_seqs].
  *  max_context_len host upper bound of context_lens (sizes the grid and the
  *                  workspace).
- * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128}, block_size
- * a power of two in [1, 1024]. */
+ * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128}, a positive
+ * finite scale, and block_size a power of two in [1, 1024]. */
 int pkv_decode_attention_paged(const void *q, int64_t q_token_stride, const void *k_cache,
                                const void *v_cache, const int32_t *block_tables,
                                int32_t max_blocks_per_seq, const int32_t *context_lens,
@@ -170,7 +176,8 @@ int pkv_decode_attention_paged(const void *q, int64_t q_token_stride, const void
                                int32_t partition_size, void *workspace, size_t workspace_bytes,
                                void *stream);
 
-/* Partition size the decode call will use for these arguments (resolves 0). */
+/* Fixed partition size the decode call will use for these arguments, or 0
+ * when it balances the work over all waves instead. */
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t max_context_len,
                                   int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t block_size, int32_t dtype,

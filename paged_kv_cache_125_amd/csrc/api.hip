@@ -38,36 +38,6 @@ bool dtype_ok(int32_t dtype) { return dtype == PKV_F32 || dtype == PKV_BF16; }
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
-// Workspace: [num_seqs][maxparts][Hq][d] fp32 accumulators, then
-// [num_seqs][maxparts][Hq][2] fp32 (max, sum), each 256-byte aligned.
-struct DecodeWs {
-    int32_t P, maxparts;
-    int64_t acc_bytes, ml_bytes, total;
-};
-
-int resolve_partition(int32_t num_seqs, int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t d,
-                      int32_t bs, int32_t dtype, int32_t requested) {
-    if (requested > 0) return requested;
-    const int32_t group = Hkv > 0 ? Hq / Hkv : 1;
-    return pkv::decode_auto_partition(num_seqs, max_ctx, Hkv, bs, dtype, d, group);
-}
-
-DecodeWs decode_ws(int32_t num_seqs, int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t d,
-                   int32_t bs, int32_t dtype, int32_t requested) {
-    DecodeWs w;
-    w.P = resolve_partition(num_seqs, max_ctx, Hq, Hkv, d, bs, dtype, requested);
-    w.maxparts = max_ctx > 0 ? (int32_t)((max_ctx + (int64_t)w.P - 1) / w.P) : 1;
-    if (w.maxparts <= 1) {
-        w.maxparts = 1;
-        w.acc_bytes = w.ml_bytes = w.total = 0;
-        return w;
-    }
-    w.acc_bytes = align256((int64_t)num_seqs * w.maxparts * Hq * d * 4);
-    w.ml_bytes = align256((int64_t)num_seqs * w.maxparts * Hq * 2 * 4);
-    w.total = w.acc_bytes + w.ml_bytes;
-    return w;
-}
-
 }  // namespace
 
 extern "C" int pkv_abi_version(void) { return PKV_ABI_VERSION; }
@@ -113,8 +83,9 @@ extern "C" int pkv_store_kvcache(const void *k, const void *v, int64_t k_token_s
 }
 
 static int check_attention_shape(const char *fn, int32_t dtype, int32_t Hq, int32_t Hkv,
-                                 int32_t d, int32_t num_seqs) {
+                                 int32_t d, int32_t num_seqs, float scale) {
     if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
+    if (!(scale > 0.f) || scale == INFINITY) return fail(PKV_EINVAL, "%s: scale must be positive and finite", fn);
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
         return fail(PKV_EINVAL, "%s: num_q_heads must be a positive multiple of num_kv_heads", fn);
     if (d != 64 && d != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim must be 64 or 128", fn);
@@ -140,7 +111,7 @@ extern "C" int pkv_prefill_attention_varlen(
     int32_t num_blocks, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, float scale, int32_t dtype, void *out, void *stream) {
     const char *fn = "pkv_prefill_attention_varlen";
-    int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs);
+    int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs, scale);
     if (rc) return rc;
     if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
         return fail(PKV_EINVAL, "%s: negative length", fn);
@@ -196,8 +167,9 @@ extern "C" int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t max_conte
                                              int32_t num_q_heads, int32_t num_kv_heads,
                                              int32_t head_dim, int32_t block_size, int32_t dtype,
                                              int32_t partition_size) {
-    return resolve_partition(num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim,
-                             block_size, dtype, partition_size);
+    const pkv::DecodePlan p = pkv::plan_decode(num_seqs, max_context_len, num_q_heads, num_kv_heads,
+                                               head_dim, block_size, dtype, partition_size);
+    return p.balanced ? 0 : p.P;
 }
 
 extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len,
@@ -205,8 +177,8 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t max_conte
                                              int32_t head_dim, int32_t block_size, int32_t dtype,
                                              int32_t partition_size) {
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-    return (size_t)decode_ws(num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim,
-                             block_size, dtype, partition_size).total;
+    return (size_t)pkv::plan_decode(num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim,
+                                    block_size, dtype, partition_size).total;
 }
 
 extern "C" int pkv_decode_attention_paged(
@@ -216,7 +188,7 @@ extern "C" int pkv_decode_attention_paged(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t dtype,
     void *out, int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream) {
     const char *fn = "pkv_decode_attention_paged";
-    int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs);
+    int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs, scale);
     if (rc) return rc;
     if (max_context_len < 0) return fail(PKV_EINVAL, "%s: negative max_context_len", fn);
     if (partition_size < 0 || partition_size % 16)
@@ -230,8 +202,8 @@ extern "C" int pkv_decode_attention_paged(
         return fail(PKV_EINVAL, "%s: q token stride smaller than a row", fn);
     if (!aligned16(q) || !aligned16(out) || (q_token_stride * es) % 16)
         return fail(PKV_EINVAL, "%s: q/out must be 16-byte aligned with 16-byte strides", fn);
-    const DecodeWs ws = decode_ws(num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim,
-                                  block_size, dtype, partition_size);
+    const pkv::DecodePlan ws = pkv::plan_decode(num_seqs, max_context_len, num_q_heads, num_kv_heads,
+                                                head_dim, block_size, dtype, partition_size);
     if ((int64_t)workspace_bytes < ws.total)
         return fail(PKV_ENOSPACE, "%s: workspace needs %lld bytes", fn, (long long)ws.total);
     if (ws.total > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
@@ -256,9 +228,11 @@ extern "C" int pkv_decode_attention_paged(
     a.out = out;
     a.P = ws.P;
     a.maxparts = ws.maxparts;
+    a.waves = ws.waves;
     a.ws_acc = ws.total ? (float *)workspace : nullptr;
     a.ws_ml = ws.total ? (float *)((char *)workspace + ws.acc_bytes) : nullptr;
-    return launched(pkv::launch_decode(a, dtype, (hipStream_t)stream), fn);
+    a.ws_cum = ws.cum_bytes ? (int32_t *)((char *)workspace + ws.acc_bytes + ws.ml_bytes) : nullptr;
+    return launched(pkv::launch_decode(a, ws, dtype, (hipStream_t)stream), fn);
 }
 
 extern "C" int pkv_upload(const void *host_buf, void *dev_buf, size_t bytes, void *stream) {

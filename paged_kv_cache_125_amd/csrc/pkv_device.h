@@ -16,6 +16,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Word 3 of a raw (stride 0) buffer resource on CDNA: 32-bit data format, so
+// buffer loads range-check against num_records and return zeros beyond it.
+constexpr int kBufWord3 = 0x00020000;
+
 // A bf16 value is the upper half of an fp32: widening is a shift or a mask.
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -75,19 +79,29 @@ __device__ __forceinline__ float shfl(float x, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
+// Exchange across lane rows with the gfx950 permlane swaps (VALU, no LDS):
+// permlane32_swap(x, x) hands each lane the values of lanes (l & 31) and
+// (l & 31) + 32; permlane16_swap(x, x) those of lanes (l & ~16) and (l | 16).
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Max / sum over a whole wave (64 lanes).
-__device__ __forceinline__ float wave_max(float x) {
-    x = row16_max(x);
-    x = fmaxf(x, shfl_xor(x, 16));
-    x = fmaxf(x, shfl_xor(x, 32));
-    return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-    x = row16_sum(x);
-    x += shfl_xor(x, 16);
-    x += shfl_xor(x, 32);
-    return x;
-}
+__device__ __forceinline__ float wave_max(float x) { return xor32_max(xor16_max(row16_max(x))); }
+__device__ __forceinline__ float wave_sum(float x) { return xor32_sum(xor16_sum(row16_sum(x))); }
 
 // Compiler-level ordering point for LDS traffic exchanged between lanes of
 // one wave (DS instructions of a wave execute in order).

@@ -31,14 +31,24 @@ struct DecodeArgs {
     void *out;
     int32_t P;                 // tokens per partition
     int32_t maxparts;          // ceil(max_context_len / P)
-    float *ws_acc;             // [num_seqs][maxparts][Hq][d]
-    float *ws_ml;              // [num_seqs][maxparts][Hq][2]  (max, sum)
+    float *ws_acc;             // fixed partitions: [num_seqs][maxparts][Hq][d]
+                               // balanced split:   [waves][2][group][d]
+    float *ws_ml;              // the matching (max, sum) pairs
+    int32_t *ws_cum;           // balanced split: chunk-count prefix sums [num_seqs + 1]
+    int32_t waves;             // balanced split: waves in the grid
 };
+// How a decode call is carried out, and the workspace it needs (the same
+// plan serves pkv_decode_workspace_bytes and the call).
+struct DecodePlan {
+    bool balanced;             // decode_sk_kernel (work split evenly over all waves)
+    int32_t P, maxparts;       // fixed-partition kernels
+    int32_t waves;             // balanced split
+    int64_t acc_bytes, ml_bytes, cum_bytes, total;
+};
+DecodePlan plan_decode(int32_t num_seqs, int32_t max_ctx, int32_t Hq, int32_t Hkv, int32_t d,
+                       int32_t bs, int dtype, int32_t partition_size);
 // Returns hipErrorNotSupported when no kernel covers the shape/dtype.
-hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t stream);
-int32_t decode_auto_partition(int32_t num_seqs, int32_t max_ctx, int32_t Hkv, int32_t bs,
-                              int dtype, int32_t d, int32_t group);
-bool decode_has_mfma_path(int dtype, int32_t d, int32_t group);
+hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &plan, int dtype, hipStream_t stream);
 
 struct PrefillArgs {
     const void *q;

@@ -139,10 +139,18 @@ def test_device_calls_validate_before_launch():
 
 
 def test_decode_workspace_and_partition():
-    P = pkv.decode_partition_size(512, 32768, 32, 8, 128, 256, torch.bfloat16)
-    assert P % 16 == 0 and P > 0
+    # bf16, head_dim 128, block-aligned pool: work balanced over all waves, no
+    # fixed partitions; the workspace holds two partial slots per wave
+    assert pkv.decode_partition_size(512, 32768, 32, 8, 128, 256, torch.bfloat16) == 0
     n = pkv.decode_workspace_bytes(512, 32768, 32, 8, 128, 256, torch.bfloat16)
-    parts = -(-32768 // P)
-    assert n >= 512 * parts * 32 * 130 * 4
+    assert n >= 8 * 2 * 4 * 130 * 4 + 513 * 4
+    # an explicit partition size selects fixed partitions
+    P = pkv.decode_partition_size(512, 32768, 32, 8, 128, 256, torch.bfloat16, 512)
+    assert P == 512
+    n = pkv.decode_workspace_bytes(512, 32768, 32, 8, 128, 256, torch.bfloat16, 512)
+    assert n >= 512 * 64 * 32 * 130 * 4
+    # small blocks: fixed partitions chosen by the library
+    P = pkv.decode_partition_size(64, 4096, 16, 8, 128, 16, torch.bfloat16)
+    assert P % 16 == 0 and P > 0
     assert pkv.decode_workspace_bytes(4, 100, 4, 2, 64, 16, torch.float32, 256) == 0
     assert pkv.decode_partition_size(4, 100, 4, 2, 64, 16, torch.float32, 48) == 48

@@ -98,6 +98,9 @@ DECODE_EDGES = [
     ([70, 9], 4, 4, 64, 16, torch.bfloat16, 16),               # head_dim 64 bf16
     ([129, 40], 8, 2, 128, 32, torch.float32, 64),             # fp32, head_dim 128
     ([1000, 1], 16, 8, 128, 2, torch.bfloat16, 0),             # block size 2, 1-token context
+    ([100, 33, 64, 1, 2049], 32, 2, 128, 32, torch.bfloat16, 0),  # group 16, block size 32
+    ([700, 31, 32, 33], 16, 8, 128, 1024, torch.bfloat16, 128),  # partitions inside one block
+    ([5000, 257], 8, 8, 128, 64, torch.bfloat16, 4096),          # P = 64 blocks (lane 63 entry)
 ]
 
 
@@ -230,3 +233,40 @@ def test_empty_batch_is_noop(cuda):
                                      torch.zeros(0, dtype=torch.int32, device="cuda"), 0, 0.125)
     torch.cuda.synchronize()
     assert out.shape == (0, 4, 64) and torch.count_nonzero(kc) == 0
+
+
+@pytest.mark.parametrize("waves", [4, 12, 64, 2048])
+def test_balanced_decode_any_wave_count(cuda, waves, monkeypatch):
+    # The balanced split cuts the (sequence, kv head, chunk) list at wave
+    # boundaries that depend on the wave count; every cut must combine back.
+    say(f"[gpu] balanced decode with {waves} waves")
+    monkeypatch.setenv("PKV_DECODE_WAVES", str(waves))
+    lens = [1, 64, 65, 700, 129, 2000, 63, 257]
+    w = custom_workload(phase="decode", seq_lens=lens, num_cached=[n - 1 for n in lens],
+                        num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=256, seed=waves)
+    out, kc, vc = gpu_run(to_device(w, "cuda"))
+    want, *_ = oracle.run_workload(w)
+    err = max_abs_err(out, want)
+    say(f"  max |err| = {err:.3e}")
+    assert err <= 2e-2
+
+
+def test_balanced_decode_padded_rows(cuda):
+    say("[gpu] balanced decode with padding rows (context 0) between real ones")
+    w = custom_workload(phase="decode", seq_lens=[300, 1000], num_cached=[299, 999], num_q_heads=8,
+                        num_kv_heads=2, head_dim=128, block_size=256, seed=8)
+    wd = to_device(w, "cuda")
+    kc, vc = alloc_pool(w.num_blocks, 256, 2, 128, torch.bfloat16, "cuda")
+    write_ranges(w.hist, w.block_tables, 256, wd.k_hist, wd.v_hist, kc, vc)
+    meta = pkv.pack_decode(w.seq_lens, w.block_tables, 256)
+    pkv.store_kvcache(wd.k_new, wd.v_new, kc, vc, meta["slot_mapping"])
+    bt = meta["block_tables"]
+    pad_bt = torch.full((1, bt.shape[1]), -1, dtype=torch.int32, device="cuda")
+    bt3 = torch.cat([bt[:1], pad_bt, bt[1:], pad_bt])
+    ctx = torch.tensor([300, 0, 1000, 0], dtype=torch.int32, device="cuda")
+    q = torch.cat([wd.q[:1], torch.ones_like(wd.q[:1]), wd.q[1:], torch.ones_like(wd.q[:1])])
+    out = pkv.decode_attention_paged(q, kc, vc, bt3, ctx, 1000, w.scale)
+    torch.cuda.synchronize()
+    want, *_ = oracle.run_workload(w)
+    assert max_abs_err(out[[0, 2]], want) <= 2e-2
+    assert torch.count_nonzero(out[[1, 3]].float()) == 0

@@ -284,3 +284,30 @@ def custom_workload(*, phase: str, seq_lens: List[int], num_cached: List[int],
                  seq_lens=list(seq_lens), num_cached=list(num_cached), block_tables=tables,
                  hist=hist, use_block_tables=use_block_tables, seed=seed)
     return _fill_values(w, device)
+
+
+def restrict(w: Workload, seq_ids: List[int], device: str = "cpu", values: bool = True) -> Workload:
+    """A workload with only the sequences ``seq_ids`` of ``w`` (same shapes,
+    block ids renumbered compactly in order of first use, fresh values drawn
+    from w's seed). Used to take a bounded sample of a large preset."""
+    remap = {}
+    tables = []
+    for s in seq_ids:
+        t = []
+        for b in w.block_tables[s]:
+            remap.setdefault(b, len(remap))
+            t.append(remap[b])
+        tables.append(t)
+    hist, seen = [], set()
+    for i, s in enumerate(seq_ids):
+        c = w.num_cached[s]
+        if c > 0:
+            key = tuple(tables[i][:_blocks_for(c, w.block_size)])
+            if key not in seen:
+                seen.add(key)
+                hist.append((i, 0, c))
+    r = dataclasses.replace(
+        w, seq_lens=[w.seq_lens[s] for s in seq_ids], num_cached=[w.num_cached[s] for s in seq_ids],
+        block_tables=tables, num_blocks=len(remap), hist=hist,
+        q=None, k_new=None, v_new=None, k_hist=None, v_hist=None)
+    return _fill_values(r, device) if values else r
