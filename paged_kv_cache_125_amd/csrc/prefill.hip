@@ -11,10 +11,11 @@
 // "KV-Cache … 是什么？").
 //
 // prefill_mfma_kernel (bf16, head_dim 128) is a FlashAttention-2 style forward
-// (Dao, 2023) laid out for CDNA4: a workgroup of 4 waves owns 128 query rows of
-// one head (32 per wave) and streams 64-key tiles of K and V through two LDS
-// buffers (the next tile's global loads are in flight while the current one
-// is computed; one barrier per tile). Both contractions run on
+// (Dao, 2023) laid out for CDNA4: a workgroup of 2 waves owns 128 query rows of
+// one head (64 per wave, as two 32-row blocks that share every K and V operand
+// read from LDS) and streams 64-key tiles of K and V through two LDS buffers
+// (the next tile's global loads are in flight while the current one is
+// computed; one barrier per tile). One wave per SIMD, two workgroups per CU. Both contractions run on
 // v_mfma_f32_32x32x16_bf16 in the transposed form
 //     S^T = K Q^T        (keys as MFMA rows, the wave's queries as columns)
 //     O^T += V^T P^T     (head dims as rows, queries as columns)
@@ -24,6 +25,8 @@
 // produced. V stays row-major in LDS; the V^T operand comes from the gfx950
 // transpose read (ds_read_b64_tr_b16), two reads of 4 consecutive keys per
 // MFMA. A wave skips key tiles that lie entirely above its causal diagonal.
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -32,7 +35,6 @@ namespace pkv {
 constexpr int kPfD = 128;
 constexpr int kPfBM = 128;     // query rows per workgroup
 constexpr int kPfBN = 64;      // keys per tile
-constexpr int kPitch = 144;    // LDS row pitch of the K and V tiles (elements)
 constexpr float kLazy = 8.f;   // log2 headroom before the running max is moved
 
 // Element offset of key `key` of sequence s in its source (k rows or the
@@ -50,21 +52,57 @@ __device__ __forceinline__ int64_t prefill_key_off(const PrefillArgs &a, int s, 
 
 // Where a 64-key tile of K/V comes from.
 enum KeySource {
-    kContiguous = 0,   // the call's k/v rows: one descriptor per sequence
+    kContiguous = 0,   // the call's k/v rows: one descriptor per tile
     kPoolBlocks = 1,   // the pool, block_size a multiple of 64: one descriptor per tile
-    kPoolSmall = 2     // the pool, smaller blocks: a block-table read per key
+    kPoolSmall = 2     // the pool, block_size 4..32: one descriptor per 4 keys
 };
 
+// LDS tile layout: 64 keys x 256 bytes, no padding; the 16-byte chunk c of key
+// row t sits at chunk position c ^ tile_swz(t). With this swizzle the K
+// operand reads (16 rows, one chunk each) and the V transpose reads (4 rows x
+// 4 chunks per 32 lanes) each touch 16 distinct chunk positions, so neither
+// has LDS bank conflicts.
+__device__ __forceinline__ int tile_swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+
+// acc *= s in place, element by element through one VGPR. Written with AGPR
+// operands so that the output accumulators stay in the accumulation registers
+// across the key loop (a plain multiply would make the compiler copy all of
+// them out to VGPRs and back on every tile, for a rescale that rarely runs).
+__device__ __forceinline__ void scale_acc(f32x16 &acc, float s) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float x = acc[r], t;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(t) : "v"(s));
+        acc[r] = x;
+    }
+}
+
 template <int SRC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_mfma_kernel(PrefillArgs a) {
-    // Two LDS buffers, each a K tile and a V tile [64 keys][kPitch], row-major.
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kPfBN * kPitch];
+    // Two buffers, each a K tile followed by a V tile, 64 keys x 256 bytes each.
+    constexpr int kTileBytes = kPfBN * 256;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * kTileBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = blockIdx.x, s = blockIdx.y;
-    const int qt = gridDim.z - 1 - blockIdx.z;   // longest (last) query tiles first
+    // Work order, XCD-aware. The hardware hands workgroup p to XCD p % 8, and
+    // each XCD has its own L2. Work is grouped by (sequence, kv head) pair,
+    // the unit that shares K and V; pair pi runs on XCD pi % 8, so all query
+    // blocks and all query heads of that kv head read their K/V tiles through
+    // one L2. Within a pair: the last (longest) query blocks first, the
+    // group's heads side by side.
+    const int qblocks = (a.max_seqlen_q + kPfBM - 1) / kPfBM;
+    const int per_pair = qblocks * a.group;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int lp = local / per_pair, within = local - lp * per_pair;
+    const int pair = 8 * lp + xcd;
+    if (pair >= a.num_seqs * a.Hkv) return;
+    const int s = pair / a.Hkv;
+    const int kvh = pair - s * a.Hkv;
+    const int qt = qblocks - 1 - within / a.group;
+    const int h = kvh * a.group + (within - (within / a.group) * a.group);
     const int q_start = a.cu_q[s];
     const int Lq = a.cu_q[s + 1] - q_start;
     const int q0 = qt * kPfBM;
@@ -72,56 +110,66 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int k_start = a.cu_k[s];
     const int Lk = a.cu_k[s + 1] - k_start;
     const int off = Lk - Lq;
-    const int kvh = h / a.group;
     const int r32 = lane & 31, j = lane >> 5;
-    const int my_row = q0 + 32 * wave + r32;
-    const bool row_ok = my_row < Lq;
-    const int my_pos = off + my_row;
-
-    // B operand of S^T = K Q^T: lane holds Q[row r32][d = 16*kk + 8*j .. +8].
-    bf16x8 qb[8];
-    {
-        const uint16_t *q = (const uint16_t *)a.q + (int64_t)(q_start + my_row) * a.q_stride +
+    // The wave owns rows q0 + 64*wave + 32*rb + r32, rb = 0, 1.
+    int my_pos[2];
+    bool row_ok[2];
+    bf16x8 qb[2][8];   // B operand of S^T = K Q^T: Q[row][d = 16*kk + 8*j .. +8]
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = q0 + 64 * wave + 32 * rb + r32;
+        row_ok[rb] = row < Lq;
+        my_pos[rb] = off + row;
+        const uint16_t *q = (const uint16_t *)a.q + (int64_t)(q_start + row) * a.q_stride +
                             (int64_t)h * kPfD + 8 * j;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
             u32x4 w = {0u, 0u, 0u, 0u};
-            if (row_ok) w = ld16(q + 16 * kk);
-            qb[kk] = __builtin_bit_cast(bf16x8, w);
+            if (row_ok[rb]) w = ld16(q + 16 * kk);
+            qb[rb][kk] = __builtin_bit_cast(bf16x8, w);
         }
     }
     const int kend = min(Lk, off + min(q0 + kPfBM, Lq));   // keys this block needs
     const int n_kt = (kend + kPfBN - 1) / kPfBN;
-    const int wave_pos0 = off + q0 + 32 * wave;            // the wave's first row position
-    const int wave_pos1 = wave_pos0 + 31;                  // ... and its last
+    const int pos_first = off + q0 + 64 * wave;           // position of the wave's first row
 
-    // Tile loader: thread -> keys (tid/16 + 16*it), 16-byte chunk tid%16, for
-    // K and V. Keys at or past kend read as zeros (buffer range check).
+    // Tile loads go global -> LDS directly (buffer_load_dwordx4 ... lds), no
+    // registers in between. Instruction i of wave w fills LDS bytes
+    // [1024*(8w+i), +1024) of a tile: keys 4*(8w+i) + lane/16, chunk position
+    // lane%16. Keys at or past kend are outside the descriptor's range and
+    // arrive as zeros.
     const uint8_t *kbase = (const uint8_t *)(SRC == kContiguous ? a.k : a.kc) + (int64_t)kvh * kPfD * 2;
     const uint8_t *vbase = (const uint8_t *)(SRC == kContiguous ? a.v : a.vc) + (int64_t)kvh * kPfD * 2;
     const uint32_t stride_b = (uint32_t)(SRC == kContiguous ? a.kv_stride * 2 : (int64_t)a.Hkv * kPfD * 2);
-    const uint32_t lane_off = (uint32_t)(tid >> 4) * stride_b + (uint32_t)(tid & 15) * 16u;
     const int32_t *bt_row = a.bt + (int64_t)s * a.maxb;
-    u32x4 kreg[4], vreg[4];
-    auto load_tile = [&](int k0) {
+    int voff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = 4 * (8 * wave + i) + (lane >> 4);
+        const int chunk = (lane & 15) ^ tile_swz(t);
+        voff[i] = (SRC == kPoolSmall ? (lane >> 4) : t) * (int)stride_b + 16 * chunk;
+    }
+    typedef __attribute__((address_space(3))) void lds_t;
+    auto load_tile = [&](int k0, uint8_t *dst) {
+        uint8_t *kd = dst + 1024 * 8 * wave;
+        uint8_t *vd = dst + kTileBytes + 1024 * 8 * wave;
         if constexpr (SRC == kPoolSmall) {
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int key = k0 + (tid >> 4) + 16 * it;
-                u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-                if (key < kend) {
-                    const int64_t eo = prefill_key_off(a, s, k_start, key, kvh, kPfD);
-                    if (eo >= 0) {
-                        kw = ld16((const uint8_t *)a.kc + eo * 2 + (tid & 15) * 16);
-                        vw = ld16((const uint8_t *)a.vc + eo * 2 + (tid & 15) * 16);
-                    }
-                }
-                kreg[it] = kw;
-                vreg[it] = vw;
+            for (int i = 0; i < 8; ++i) {
+                const int key0 = k0 + 4 * (8 * wave + i);
+                const int lb = key0 >> a.log2bs;
+                const int blk = (key0 < kend && lb < a.maxb) ? bt_row[lb] : -1;
+                const bool ok = blk >= 0 && blk < a.num_blocks;
+                const int nrec = ok ? min(4, kend - key0) * (int)stride_b : 0;
+                const int64_t rb_ = ok ? ((int64_t)blk * a.bs + (key0 & (a.bs - 1))) * stride_b : 0;
+                const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + rb_), (short)0, nrec, kBufWord3);
+                const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + rb_), (short)0, nrec, kBufWord3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_t *)(kd + 1024 * i), 16, voff[i], 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_t *)(vd + 1024 * i), 16, voff[i], 0, 0, 0);
             }
         } else {
             const int valid = min(kPfBN, kend - k0);
-            int64_t row0;   // first row of the tile in its source
+            int64_t row0;   // first key row of the tile in its source
             bool ok = valid > 0;
             if constexpr (SRC == kContiguous) {
                 row0 = (int64_t)k_start + k0;
@@ -132,146 +180,190 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 row0 = (int64_t)blk * a.bs + (k0 & (a.bs - 1));
             }
             const int nrec = ok ? valid * (int)stride_b : 0;
-            const int64_t rb = ok ? row0 * stride_b : 0;
-            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + rb), (short)0, nrec, kBufWord3);
-            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + rb), (short)0, nrec, kBufWord3);
+            const int64_t rb_ = ok ? row0 * stride_b : 0;
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + rb_), (short)0, nrec, kBufWord3);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + rb_), (short)0, nrec, kBufWord3);
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int o = (int)(lane_off + (uint32_t)(16 * it) * stride_b);
-                kreg[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
-                vreg[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_t *)(kd + 1024 * i), 16, voff[i], 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_t *)(vd + 1024 * i), 16, voff[i], 0, 0, 0);
             }
         }
     };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int o = ((tid >> 4) + 16 * it) * kPitch + 8 * (tid & 15);
-            *reinterpret_cast<u32x4 *>(&lds[buf][0][o]) = kreg[it];
-            *reinterpret_cast<u32x4 *>(&lds[buf][1][o]) = vreg[it];
-        }
-    };
 
-    float m = -INFINITY, l = 0.f;
-    f32x16 o[4];
+    // Per-lane LDS byte offsets of the operand reads (loop invariant).
+    // K (A operand of S^T = K Q^T): key row 32*mt + r32, chunk 2*kk + j.
+    int koff[8];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int kk = 0; kk < 8; ++kk) koff[kk] = r32 * 256 + 16 * ((2 * kk + j) ^ tile_swz(r32));
+    // V^T (A operand of O^T += V^T P^T) by transpose reads: lane reads 4
+    // elements of key row 32*mt + 16*ap + 4*j + q16/4 (+8 for the upper
+    // half), dims 32*nt + 16*g2 + 4*(q16%4) .. +4.
+    const int q16 = lane & 15, g2 = (lane >> 4) & 1;
+    int voffr[2][4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[nt][r] = 0.f;
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int t = 4 * j + 8 * hi + (q16 >> 2);
+            const int chunk = 4 * nt + 2 * g2 + ((q16 & 3) >> 1);
+            voffr[hi][nt] = t * 256 + 16 * (chunk ^ tile_swz(t)) + 8 * (q16 & 1);
+        }
+
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    f32x16 o[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[rb][nt][r] = 0.f;
     const float c = a.scale_log2;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int k0 = kt * kPfBN;
-        const int buf = kt & 1;
-        if (kt + 1 < n_kt) load_tile(k0 + kPfBN);
-        const uint16_t *Ks = lds[buf][0];
-        const uint16_t *Vs = lds[buf][1];
-        if (k0 <= wave_pos1) {   // some key of the tile is visible to some row of the wave
-            // S^T tiles: st[mt][r] = S[row r32][key k0 + 32*mt + 8*(r/4) + 4*j + r%4].
-            f32x16 st[2];
+    // One key tile: start the direct loads of the next tile into `nxt`, then
+    // compute on `cur`. The two buffers are distinct objects (restrict), which
+    // lets the compiler read `cur` without waiting for the loads into `nxt`.
+    auto tile_step = [&](auto masked, const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
+                         int k0, bool more) {
+        if (more) load_tile(k0 + kPfBN, nxt);
+        const uint8_t *Ks = cur;
+        const uint8_t *Vs = cur + kTileBytes;
+        // No tile is skipped: a tile that lies above some of the wave's rows
+        // (at most the last one of the block) only brings masked scores, which
+        // add nothing, and the wave would wait at the barrier anyway. Keeping
+        // the loop body free of branches around the accumulators keeps them
+        // in place across iterations.
+        {
+            // S^T tiles: st[rb][mt][r] = S[row r32 of block rb][key k0 + 32*mt + 8*(r/4) + 4*j + r%4].
+            // Every K operand read from LDS feeds both row blocks.
+            f32x16 st[2][2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) st[mt][r] = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const u32x4 ka = *reinterpret_cast<const u32x4 *>(
-                        &Ks[(32 * mt + r32) * kPitch + 16 * kk + 8 * j]);
-                    st[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka),
-                                                                     qb[kk], st[mt], 0, 0, 0);
-                }
-            }
-            // Causal mask on the tiles that cross the wave's diagonal: key
-            // k0 + 32*mt + 8*(r/4) + 4*j + r%4 is hidden when its in-tile
-            // offset exceeds lim = my_pos - k0 - 4*j.
-            if (row_ok && k0 + kPfBN - 1 > wave_pos0) {
-                const int lim = my_pos - k0 - 4 * j;
+            for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * mt + 8 * (r >> 2) + (r & 3) > lim) st[mt][r] = -INFINITY;
-            }
-            // Online softmax in the exp2 domain on raw scores: the max is taken
-            // on q.k, and p = exp2(q.k * c - m * c) with c = scale * log2(e) is
-            // one FMA feeding v_exp_f32. The running max m is moved (and O, l
-            // rescaled) only when some row's tile max exceeds it by more than
-            // kLazy / c, so p <= 2^kLazy; the final division by l makes the
-            // result independent of when the rescales happened.
-            float mx = -INFINITY;
+                    for (int r = 0; r < 16; ++r) st[rb][mt][r] = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, st[mt][r]), st[mt][r + 1]);
-            mx = xor32_max(mx);
-            const bool grow = mx * c > m * c + kLazy;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // the decision is wave-wide
-                const float m_new = fmaxf(m, mx);
-                const float alpha = m == m_new ? 1.f : fast_exp2((m - m_new) * c);
-                l *= alpha;
+                for (int kk = 0; kk < 8; ++kk) {
+                    const bf16x8 kab = __builtin_bit_cast(bf16x8,
+                        *reinterpret_cast<const u32x4 *>(Ks + 32 * 256 * mt + koff[kk]));
+                    st[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kab, qb[0][kk], st[0][mt], 0, 0, 0);
+                    st[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kab, qb[1][kk], st[1][mt], 0, 0, 0);
+                }
+            // Online softmax: causal mask (diagonal tiles only), max on raw
+            // scores, one lazy-rescale decision for both row blocks, then
+            // p = exp2(q.k * c - m * c) rounded to bf16 and row sums of the
+            // rounded p via v_dot2.
+            float mx[2];
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+            for (int rb = 0; rb < 2; ++rb) {
+                if constexpr (decltype(masked)::value) {
+                    const int lim = my_pos[rb] - k0 - 4 * j;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[nt][r] *= alpha;
-                m = m_new;
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            st[rb][mt][r] = (32 * mt + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : st[rb][mt][r];
+                }
+                float x = -INFINITY;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2)
+                        x = fmaxf(fmaxf(x, st[rb][mt][r]), st[rb][mt][r + 1]);
+                mx[rb] = xor32_max(x);
             }
-            const float mc = m * c;
-
-            // O^T += V^T P^T over 4 steps of 16 keys. In step (mt, ap) lane
-            // half j supplies keys 32*mt + 16*ap + 8*(e/4) + 4*j + e%4, e = 0..7:
-            // its own S^T registers 8*ap .. 8*ap+7, and two transpose reads of
-            // 4 consecutive V rows for the A operand. The row sum l adds the
-            // same bf16-rounded weights that enter the MFMA (v_dot2 with ones).
-            const int q16 = lane & 15, g2 = (lane >> 4) & 1;
+            if (__builtin_amdgcn_ballot_w64(mx[0] * c > m[0] * c + kLazy || mx[1] * c > m[1] * c + kLazy) != 0) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    const float m_new = fmaxf(m[rb], mx[rb]);
+                    const float alpha = m[rb] == m_new ? 1.f : fast_exp2((m[rb] - m_new) * c);
+                    l[rb] *= alpha;
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) scale_acc(o[rb][nt], alpha);
+                    m[rb] = m_new;
+                }
+            }
+            bf16x8 pb[2][2][2];   // [rb][mt][ap]
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const float mc = m[rb] * c;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int ap = 0; ap < 2; ++ap) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            pb[rb][mt][ap][e] = (__bf16)fast_exp2(__builtin_fmaf(st[rb][mt][8 * ap + e], c, -mc));
+#pragma unroll
+                        for (int e = 0; e < 8; e += 2)
+                            l[rb] = __builtin_amdgcn_fdot2_f32_bf16(
+                                bf16x2{pb[rb][mt][ap][e], pb[rb][mt][ap][e + 1]}, ones, l[rb], false);
+                    }
+            }
+            // O^T += V^T P^T over 4 steps of 16 keys; each V^T operand (two
+            // transpose reads of 4 consecutive key rows) feeds both row blocks.
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int ap = 0; ap < 2; ++ap) {
-                    bf16x8 pb;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        pb[e] = (__bf16)fast_exp2(__builtin_fmaf(st[mt][8 * ap + e], c, -mc));
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2)
-                        l = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e], pb[e + 1]}, ones, l, false);
-                    const int t_lo = 32 * mt + 16 * ap + 4 * j + (q16 >> 2);
-                    const uint16_t *src_lo = Vs + t_lo * kPitch + 16 * g2 + 4 * (q16 & 3);
-                    const uint16_t *src_hi = src_lo + 8 * kPitch;
+                    const uint8_t *vrow = Vs + (32 * mt + 16 * ap) * 256;
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) {
                         typedef short s16x4 __attribute__((ext_vector_type(4)));
-                        typedef short s16x8 __attribute__((ext_vector_type(8)));
                         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4 *)(src_lo + 32 * nt));
+                            (__attribute__((address_space(3))) s16x4 *)(vrow + voffr[0][nt]));
                         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4 *)(src_hi + 32 * nt));
-                        const s16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, av), pb, o[nt], 0, 0, 0);
+                            (__attribute__((address_space(3))) s16x4 *)(vrow + voffr[1][nt]));
+                        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        o[0][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[0][mt][ap], o[0][nt], 0, 0, 0);
+                        o[1][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[1][mt][ap], o[1][nt], 0, 0, 0);
                     }
                 }
         }
-        if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    };
+
+    load_tile(0, lds[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Tiles below every row's diagonal need no mask; the last few do.
+    const int n_full = min(n_kt, max(0, (off + q0 + 1) / kPfBN));
+    int kt = 0;
+    for (; kt < n_full; ++kt) {
+        const int buf = kt & 1;
+        // The other buffer was last read before the previous barrier.
+        tile_step(std::false_type{}, lds[buf], lds[buf ^ 1], kt * kPfBN, kt + 1 < n_kt);
+        // The next tile's direct loads must have landed before the barrier
+        // hands its buffer to the other wave.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    for (; kt < n_kt; ++kt) {
+        const int buf = kt & 1;
+        tile_step(std::true_type{}, lds[buf], lds[buf ^ 1], kt * kPfBN, kt + 1 < n_kt);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    l = xor32_sum(l);
-    if (row_ok) {
-        const float inv = 1.f / l;
-        uint16_t *out = (uint16_t *)a.out + ((int64_t)(q_start + my_row) * a.Hq + h) * kPfD;
-        // o[nt][4*g + c] = O[row][d = 32*nt + 8*g + 4*j + c]
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float lt = xor32_sum(l[rb]);
+        if (!row_ok[rb]) continue;
+        const float inv = 1.f / lt;
+        const int row = q0 + 64 * wave + 32 * rb + r32;
+        uint16_t *out = (uint16_t *)a.out + ((int64_t)(q_start + row) * a.Hq + h) * kPfD;
+        // o[rb][nt][4*g + c] = O[row][d = 32*nt + 8*g + 4*j + c]
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 u32x2 w;
-                w[0] = pack_bf16x2(o[nt][4 * g] * inv, o[nt][4 * g + 1] * inv);
-                w[1] = pack_bf16x2(o[nt][4 * g + 2] * inv, o[nt][4 * g + 3] * inv);
+                w[0] = pack_bf16x2(o[rb][nt][4 * g] * inv, o[rb][nt][4 * g + 1] * inv);
+                w[1] = pack_bf16x2(o[rb][nt][4 * g + 2] * inv, o[rb][nt][4 * g + 3] * inv);
                 *reinterpret_cast<u32x2 *>(out + 32 * nt + 8 * g + 4 * j) = w;
             }
     }
@@ -346,14 +438,21 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
     if (a.num_seqs == 0 || a.max_seqlen_q == 0) return hipSuccess;
-    if (dtype == 1 && a.d == 128) {
-        const dim3 grid(a.Hq, a.num_seqs, (a.max_seqlen_q + kPfBM - 1) / kPfBM);
+    // The MFMA kernel's direct tile loads address up to 64 key rows per
+    // descriptor with 32-bit offsets, and the small-block form needs blocks of
+    // at least 4 keys; anything else takes the generic kernel.
+    const int64_t row_bytes = a.paged ? (int64_t)a.Hkv * a.d * 2 : a.kv_stride * 2;
+    if (dtype == 1 && a.d == 128 && (!a.paged || a.bs >= 4) && row_bytes * kPfBN < (1ll << 31)) {
+        const int64_t pairs = (int64_t)a.num_seqs * a.Hkv;
+        const int64_t nwg = 8 * ((pairs + 7) / 8) * ((a.max_seqlen_q + kPfBM - 1) / kPfBM) * a.group;
+        if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)nwg);
         if (!a.paged)
-            hipLaunchKernelGGL(prefill_mfma_kernel<kContiguous>, grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(prefill_mfma_kernel<kContiguous>, grid, dim3(128), 0, stream, a);
         else if (a.bs % kPfBN == 0)
-            hipLaunchKernelGGL(prefill_mfma_kernel<kPoolBlocks>, grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(prefill_mfma_kernel<kPoolBlocks>, grid, dim3(128), 0, stream, a);
         else
-            hipLaunchKernelGGL(prefill_mfma_kernel<kPoolSmall>, grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(prefill_mfma_kernel<kPoolSmall>, grid, dim3(128), 0, stream, a);
     } else {
         const dim3 grid((a.max_seqlen_q + 3) / 4, a.Hq, a.num_seqs);
         if (dtype == 0 && a.d == 64)
@@ -362,6 +461,9 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
             hipLaunchKernelGGL((prefill_generic_kernel<float, 128>), grid, dim3(256), 0, stream, a);
         else if (dtype == 1 && a.d == 64)
             hipLaunchKernelGGL((prefill_generic_kernel<uint16_t, 64>), grid, dim3(256), 0, stream,
+                               a);
+        else if (dtype == 1 && a.d == 128)
+            hipLaunchKernelGGL((prefill_generic_kernel<uint16_t, 128>), grid, dim3(256), 0, stream,
                                a);
         else
             return hipErrorNotSupported;

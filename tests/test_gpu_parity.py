@@ -128,6 +128,8 @@ PREFILL_EDGES = [
     ([40, 100], [32, 0], 4, 2, 64, 8, torch.float32, True),                       # fp32 d64 prefix
     ([1], [0], 8, 8, 128, 16, torch.bfloat16, False),                             # one token
     ([17, 18], [16, 16], 4, 2, 128, 16, torch.bfloat16, True),                    # Lq 1 and 2
+    ([150, 70], [64, 0], 8, 4, 128, 2, torch.bfloat16, True),                     # blocks of 2 keys
+    ([600, 129, 64], [320, 64, 0], 8, 2, 128, 64, torch.bfloat16, True),          # blocks of 64 keys
 ]
 
 
