@@ -117,16 +117,31 @@ class Part:
                                                        w.block_size, w.dtype)
         self.names = ["pack", "store", "attention"]
         self.times = {n: [] for n in self.names}
+        self.ring = []
         torch.cuda.synchronize()
 
+    def prepare(self, n):
+        """n (pinned host, device) metadata buffers, one per pass, so that the
+        passes allocate nothing (a new pinned allocation can stall the host)."""
+        pkv, s = self.pkv, self.s
+        if self.phase == "decode":
+            meta = pkv.pack_decode(s.seq_lens, s.block_tables, s.block_size, device="cpu")
+        else:
+            meta = pkv.pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size, device="cpu")
+        nbytes = int(meta["layout"].total_bytes)
+        self.ring = [(torch.empty(nbytes, dtype=torch.uint8, pin_memory=True),
+                      torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(n)]
+
     def run(self, i, events):
-        """One pass; events is a list of 4 torch.cuda.Event or None."""
+        """Pass i (each pass has its own metadata buffers); events is a list of
+        4 torch.cuda.Event or None."""
         pkv, s = self.pkv, self.s
         w, kc, vc, out = self.copies[i % len(self.copies)]
+        hb, db = self.ring[i]
         rec = (lambda j: events[j].record()) if events else (lambda j: None)
         rec(0)
         if self.phase == "decode":
-            meta = pkv.pack_decode(s.seq_lens, s.block_tables, s.block_size)
+            meta = pkv.pack_decode(s.seq_lens, s.block_tables, s.block_size, host_buffer=hb, dev_buffer=db)
             rec(1)
             pkv.store_kvcache(w.k_new, w.v_new, kc, vc, meta["slot_mapping"])
             rec(2)
@@ -134,7 +149,8 @@ class Part:
                                        meta["max_seqlen_k"], s.scale, out=out, workspace=self.ws)
             rec(3)
         else:
-            meta = pkv.pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size)
+            meta = pkv.pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size,
+                                    host_buffer=hb, dev_buffer=db)
             rec(1)
             pkv.store_kvcache(w.k_new, w.v_new, kc, vc, meta["slot_mapping"])
             rec(2)
@@ -183,14 +199,17 @@ class Part:
 # ----------------------------------------------------------------- oracle side
 
 def cpu_baseline(phase, preset, budget_s):
-    """The oracle, as it stands, on the host cores: store + attention of the
-    preset (decode: every sequence; prefill: as many whole sequences as fit
-    the time budget), repeated while the budget allows. Returns the rate in the
-    unit of the GPU figure (GB/s for decode, TFLOP/s for prefill)."""
+    """The oracle, as it stands, on the host cores, over a bounded sample of
+    the preset: whole sequences from the front of the batch, each run through
+    the oracle's store and attention exactly as the GPU step runs them
+    (prefix-hit sequences read their keys through the block tables), repeated
+    until the time budget is spent. Returns the rate in the unit of the GPU
+    figure (GB/s for decode, TFLOP/s for prefill)."""
     import oracle
     from workloads import make_workload, restrict
     shape = make_workload(preset, values=False)
     threads = oracle.max_threads()
+    cpu = platform.processor() or platform.machine()
     if phase == "decode":
         # whole sequences from the front of the batch, up to ~200K context tokens
         take, tot = [], 0
@@ -202,7 +221,7 @@ def cpu_baseline(phase, preset, budget_s):
         w = restrict(shape, take)
         kp, vp, slots = oracle.pools_after_store(w)     # setup: history + first write
         reps, t = 0, 0.0
-        while t < budget_s and reps < 50:
+        while t < budget_s:
             t0 = time.perf_counter()
             oracle.store(w.k_new, kp, slots)
             oracle.store(w.v_new, vp, slots)
@@ -214,32 +233,34 @@ def cpu_baseline(phase, preset, budget_s):
         return {"value": rate, "unit": "GB/s", "cores": threads, "kind": "oracle",
                 "sample": f"{len(take)} of {len(shape.seq_lens)} sequences ({tot} context tokens): "
                           f"oracle store + decode attention, {reps} repetition(s), {t:.1f} s",
-                "cpu": platform.processor() or platform.machine()}
-    w = make_workload(preset)
-    # prefill: a prefix of the batch, whole sequences, within the budget
-    from copy import copy
-    order = list(range(len(w.seq_lens)))
-    t, done, flops = 0.0, 0, 0.0
-    qo = np.concatenate([[0], np.cumsum(w.q_lens)])
-    for s in order:
-        sub = copy(w)
-        sub.seq_lens, sub.num_cached = [w.seq_lens[s]], [w.num_cached[s]]
-        sub.block_tables = [w.block_tables[s]]
-        sub.q, sub.k_new, sub.v_new = w.q[qo[s]:qo[s + 1]], w.k_new[qo[s]:qo[s + 1]], w.v_new[qo[s]:qo[s + 1]]
-        if w.num_cached[s] > 0:
-            break   # prefix presets: keep the sample to uncached sequences
+                "cpu": cpu}
+    # prefill: one sequence per oracle call, cycling over the front of the batch
+    t, flops, calls, seen = 0.0, 0.0, 0, set()
+    s = 0
+    while t < budget_s:
+        w = restrict(shape, [s])
+        kp = vp = None
+        if w.use_block_tables:
+            kp, vp, slots = oracle.pools_after_store(w)
         t0 = time.perf_counter()
-        oracle.attention(sub.q, sub.q_lens, sub.seq_lens, w.num_kv_heads, w.scale,
-                         k=sub.k_new, v=sub.v_new)
+        if w.use_block_tables:
+            oracle.store(w.k_new, kp, slots)
+            oracle.store(w.v_new, vp, slots)
+            oracle.attention(w.q, w.q_lens, w.seq_lens, w.num_kv_heads, w.scale,
+                             k_cache=kp, v_cache=vp, tables=w.block_tables, block_size=w.block_size)
+        else:
+            oracle.attention(w.q, w.q_lens, w.seq_lens, w.num_kv_heads, w.scale,
+                             k=w.k_new, v=w.v_new)
         t += time.perf_counter() - t0
-        flops += prefill_flops(sub)
-        done += 1
-        if t >= budget_s:
-            break
+        flops += prefill_flops(w)
+        calls += 1
+        seen.add(s)
+        s = (s + 1) % len(shape.seq_lens)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(w.seq_lens)} sequences of the preset, oracle prefill "
-                      f"attention, {t:.1f} s",
-            "cpu": platform.processor() or platform.machine()}
+            "sample": f"{calls} oracle prefill calls, one sequence each, over {len(seen)} of the "
+                      f"preset's {len(shape.seq_lens)} sequences (store + attention through the "
+                      f"block tables where the preset reads the cache), {t:.1f} s",
+            "cpu": cpu}
 
 
 # ----------------------------------------------------------------- traffic
@@ -291,7 +312,7 @@ def summarize_counters(fetch_dir, write_dir, workload):
 
     def calib(tab, counter):
         # the 1 GiB copies, not the small metadata uploads that share the blit kernel
-        vals = [v for k, c in tab.items() if "copy" in k.lower() for v in c.get(counter, []) if v > kib / 2]
+        vals = [v for k, c in tab.items() if "copy" in k.lower() for v in c.get(counter, []) if v > kib / 4]
         return sum(vals) / len(vals) if vals else None
 
     copy_f, copy_w = calib(f, "FETCH_SIZE"), calib(w, "WRITE_SIZE")
@@ -300,30 +321,53 @@ def summarize_counters(fetch_dir, write_dir, workload):
     ff, fw = copy_f / kib, copy_w / kib
     data = json.load(open(COUNTERS_JSON)) if os.path.exists(COUNTERS_JSON) else {}
     groups = {
-        "decode": (["decode_blk_kernel", "decode_mfma_kernel", "decode_reduce_kernel"], "decode.hip"),
+        "decode": (["decode_sk_kernel", "decode_sk_reduce_kernel", "decode_blk_kernel",
+                    "decode_mfma_kernel", "decode_generic_kernel", "decode_reduce_kernel"], "decode.hip"),
         "prefill": (["prefill_mfma_kernel"], "prefill.hip"),
-        "store": (["store_kvcache_kernel"], "store.hip"),
     }
-    presets = {p for _, p in WORKLOADS[workload]}
+    parts = WORKLOADS[workload]
     for name, (kernels, src) in groups.items():
-        fetch = sum(avg(f, k, "FETCH_SIZE") or 0.0 for k in kernels)
-        write = sum(avg(w, k, "WRITE_SIZE") or 0.0 for k in kernels)
+        # kernel names match by substring; a longer name listed later must not
+        # be counted twice under a shorter one
+        tabs = {}
+        for tab, counter in ((f, "FETCH_SIZE"), (w, "WRITE_SIZE")):
+            tot = 0.0
+            for k in kernels:
+                vals = [v for kn, c in tab.items() if k in kn and not any(
+                    o != k and k in o and o in kn for o in kernels) for v in c.get(counter, [])]
+                tot += sum(vals) / len(vals) if vals else 0.0
+            tabs[counter] = tot
+        fetch, write = tabs["FETCH_SIZE"], tabs["WRITE_SIZE"]
         if fetch == 0 and write == 0:
             continue
-        for p in presets:
+        keys = [p for ph, p in parts if ph == name]
+        for p in keys:
             data[f"{name}-preset{p}"] = {
                 "kernels": kernels, "source_sha": _source_sha(src),
                 "fetch_kib_raw": fetch, "write_kib_raw": write,
                 "copy_calibration": {"bytes": CALIBRATION_BYTES, "fetch_factor": ff, "write_factor": fw},
                 "hbm_bytes_per_launch": (fetch / ff + write / fw) * 1024,
-                "note": "mean over dispatches; the store of a step mixes its two workloads"
-                        if name == "store" and len(presets) > 1 else "mean over dispatches"}
+                "note": "mean over the dispatches of the counter run"}
     os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
     json.dump(data, open(COUNTERS_JSON, "w"), indent=1, sort_keys=True)
     print(json.dumps({k: data[k]["hbm_bytes_per_launch"] for k in sorted(data)}, indent=1))
 
 
 # ----------------------------------------------------------------- main
+
+def preroll_cycles(seconds: float) -> int:
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about
+    `seconds` (calibrated once with events), capped at 0.5 s."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)          # first launch loads the kernel
+    n = 20_000_000
+    a.record()
+    torch.cuda._sleep(n)
+    b.record()
+    b.synchronize()
+    per_cycle = max(a.elapsed_time(b) * 1e-3 / n, 1e-12)
+    return int(min(max(seconds, 1e-3), 0.5) / per_cycle)
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -368,21 +412,45 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    for p in parts:
+        p.prepare(args.warmup + args.steps)
     log("[bench] warmup")
     for i in range(args.warmup):
         metas = [p.run(i, None) for p in parts]
     torch.cuda.synchronize()
+    del metas
 
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in parts]
-              for _ in range(args.steps)]
+    # Whole steps, wall clock: host packing, uploads and every kernel, with a
+    # synchronize on both sides.
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     keep = []
     for i in range(args.steps):
-        keep.append([p.run(i, events[i][j]) for j, p in enumerate(parts)])
+        keep.append([p.run(args.warmup + i, None) for p in parts])
+    t_host = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    del keep
+    # The same steps again, each call bracketed by HIP events on its stream.
+    # The host enqueues them while a short spin kernel holds the GPU, so the
+    # kernels run back to back and no interval contains host launch latency.
+    for p in parts:
+        p.prepare(args.steps)
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in parts]
+              for _ in range(args.steps)]
+    preroll = preroll_cycles(3 * t_host + 5e-3)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(preroll)
+    t_enq = time.perf_counter()
+    keep = []
+    for i in range(args.steps):
+        keep.append([p.run(i, events[i][j]) for j, p in enumerate(parts)])
+    t_enq = time.perf_counter() - t_enq
+    torch.cuda.synchronize()
+    gpu_span = events[0][0][0].elapsed_time(events[-1][-1][3]) * 1e-3
+    log(f"[bench] wall {wall * 1e3:.2f} ms for {args.steps} steps (host {t_host * 1e3:.1f} ms); "
+        f"event pass: host enqueue {t_enq * 1e3:.1f} ms, gpu span {gpu_span * 1e3:.2f} ms")
     del keep
     for j, p in enumerate(parts):
         p.collect([events[i][j] for i in range(args.steps)])
@@ -403,7 +471,9 @@ def main():
         roof = {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": value / HBM_PEAK_GBS,
                 "traffic": counters_traffic("decode.hip", f"decode-preset{dec['preset']}"),
-                "kernel": "decode_mfma_kernel + decode_reduce_kernel (one decode_attention_paged call)",
+                "kernel": ("decode_sk_kernel + decode_sk_reduce_kernel" if dec["partition_size"] == 0
+                           else "fixed-partition decode kernel + decode_reduce_kernel")
+                          + " (one decode_attention_paged call)",
                 "algorithmic_bytes_per_launch": per_launch, "avg_launch_us": dec["attention_us"]}
         cpu_main = cpu.get("decode")
     else:

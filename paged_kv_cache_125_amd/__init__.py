@@ -212,12 +212,12 @@ def decode_attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
 
 def _csr(block_tables: Sequence[Sequence[int]]):
     import numpy as np
+    lens = np.fromiter((len(t) for t in block_tables), dtype=np.int64, count=len(block_tables))
     off = np.zeros(len(block_tables) + 1, dtype=np.int64)
-    for i, t in enumerate(block_tables):
-        off[i + 1] = off[i] + len(t)
+    np.cumsum(lens, out=off[1:])
     ids = np.zeros(max(1, int(off[-1])), dtype=np.int32)
-    for i, t in enumerate(block_tables):
-        ids[off[i]:off[i + 1]] = t
+    if off[-1] > 0:
+        ids[:off[-1]] = np.concatenate([np.asarray(t, dtype=np.int32) for t in block_tables])
     return ids, off
 
 
@@ -242,7 +242,8 @@ def _views(layout: BatchLayout, dev: torch.Tensor) -> Dict[str, object]:
 
 
 def _pack(prefill: bool, seq_lens, num_cached, block_tables, block_size: int, device,
-          stream=None) -> Dict[str, object]:
+          stream=None, host_buffer: Optional[torch.Tensor] = None,
+          dev_buffer: Optional[torch.Tensor] = None) -> Dict[str, object]:
     import numpy as np
     L = lib()
     lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
@@ -256,22 +257,33 @@ def _pack(prefill: bool, seq_lens, num_cached, block_tables, block_size: int, de
     else:
         _check(L.pkv_plan_decode(len(lens), P(lens.ctypes.data), P(off.ctypes.data), block_size,
                                  ctypes.byref(layout)))
-    pinned = torch.cuda.is_available()
-    host = torch.empty(layout.total_bytes, dtype=torch.uint8, pin_memory=pinned)
+    nbytes = layout.total_bytes
+    if host_buffer is None:
+        host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=torch.cuda.is_available())
+    else:
+        if host_buffer.dtype != torch.uint8 or host_buffer.device.type != "cpu" \
+                or not host_buffer.is_contiguous() or host_buffer.numel() < nbytes:
+            raise ValueError(f"host_buffer must be a contiguous CPU uint8 tensor of >= {nbytes} bytes")
+        host = host_buffer[:nbytes]
     if prefill:
         _check(L.pkv_pack_prefill(len(lens), P(lens.ctypes.data), P(cached.ctypes.data),
                                   P(ids.ctypes.data), P(off.ctypes.data), block_size,
-                                  ctypes.byref(layout), P(host.data_ptr()), layout.total_bytes))
+                                  ctypes.byref(layout), P(host.data_ptr()), nbytes))
     else:
         _check(L.pkv_pack_decode(len(lens), P(lens.ctypes.data), P(ids.ctypes.data),
                                  P(off.ctypes.data), block_size, ctypes.byref(layout),
-                                 P(host.data_ptr()), layout.total_bytes))
+                                 P(host.data_ptr()), nbytes))
     if device is None or torch.device(device).type == "cpu":
         dev = host
     else:
-        dev = torch.empty(layout.total_bytes, dtype=torch.uint8, device=device)
-        _check(L.pkv_upload(P(host.data_ptr()), P(dev.data_ptr()), layout.total_bytes,
-                            _stream(stream)))
+        if dev_buffer is None:
+            dev = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        else:
+            if dev_buffer.dtype != torch.uint8 or dev_buffer.device.type != "cuda" \
+                    or not dev_buffer.is_contiguous() or dev_buffer.numel() < nbytes:
+                raise ValueError(f"dev_buffer must be a contiguous device uint8 tensor of >= {nbytes} bytes")
+            dev = dev_buffer[:nbytes]
+        _check(L.pkv_upload(P(host.data_ptr()), P(dev.data_ptr()), nbytes, _stream(stream)))
     res = _views(layout, dev)
     res["host_buffer"] = host   # keep the pinned source alive until the copy has run
     res["layout"] = layout
@@ -280,14 +292,23 @@ def _pack(prefill: bool, seq_lens, num_cached, block_tables, block_size: int, de
 
 def pack_prefill(seq_lens: Sequence[int], num_cached: Sequence[int],
                  block_tables: Sequence[Sequence[int]], block_size: int,
-                 device="cuda", stream=None) -> Dict[str, object]:
+                 device="cuda", stream=None, host_buffer: Optional[torch.Tensor] = None,
+                 dev_buffer: Optional[torch.Tensor] = None) -> Dict[str, object]:
     """pkv_plan_prefill + pkv_pack_prefill + pkv_upload: the step's metadata in
     one buffer. Returns device views slot_mapping, cu_seqlens_q/_k,
-    block_tables (or None) and the host scalars."""
-    return _pack(True, seq_lens, num_cached, block_tables, block_size, device, stream)
+    block_tables (or None) and the host scalars.
+
+    ``host_buffer`` (pinned CPU uint8) and ``dev_buffer`` (device uint8), when
+    given, are used as the staging and destination buffers instead of new
+    allocations; the caller must not reuse ``host_buffer`` before the stream
+    has run the copy."""
+    return _pack(True, seq_lens, num_cached, block_tables, block_size, device, stream,
+                 host_buffer, dev_buffer)
 
 
 def pack_decode(seq_lens: Sequence[int], block_tables: Sequence[Sequence[int]], block_size: int,
-                device="cuda", stream=None) -> Dict[str, object]:
-    """pkv_plan_decode + pkv_pack_decode + pkv_upload."""
-    return _pack(False, seq_lens, None, block_tables, block_size, device, stream)
+                device="cuda", stream=None, host_buffer: Optional[torch.Tensor] = None,
+                dev_buffer: Optional[torch.Tensor] = None) -> Dict[str, object]:
+    """pkv_plan_decode + pkv_pack_decode + pkv_upload (buffers as in pack_prefill)."""
+    return _pack(False, seq_lens, None, block_tables, block_size, device, stream,
+                 host_buffer, dev_buffer)
