@@ -11,11 +11,12 @@
 // "KV-Cache … 是什么？").
 //
 // prefill_mfma_kernel (bf16, head_dim 128) is a FlashAttention-2 style forward
-// (Dao, 2023) laid out for CDNA4: a workgroup of 2 waves owns 128 query rows of
-// one head (64 per wave, as two 32-row blocks that share every K and V operand
-// read from LDS) and streams 64-key tiles of K and V through two LDS buffers
-// (the next tile's global loads are in flight while the current one is
-// computed; one barrier per tile). One wave per SIMD, two workgroups per CU. Both contractions run on
+// (Dao, 2023) laid out for CDNA4: a workgroup of 4 waves owns 128 query rows of
+// one head (32 per wave) and streams 64-key tiles of K and V through two LDS
+// buffers (the next tile's global loads are in flight while the current one
+// is computed; one barrier per tile). Two workgroups per CU, so two waves
+// share each SIMD: while one waits on LDS or runs its softmax on the VALU,
+// the other keeps the matrix core busy. Both contractions run on
 // v_mfma_f32_32x32x16_bf16 in the transposed form
 //     S^T = K Q^T        (keys as MFMA rows, the wave's queries as columns)
 //     O^T += V^T P^T     (head dims as rows, queries as columns)
@@ -33,7 +34,6 @@
 namespace pkv {
 
 constexpr int kPfD = 128;
-constexpr int kPfBM = 128;     // query rows per workgroup
 constexpr int kPfBN = 64;      // keys per tile
 constexpr float kLazy = 8.f;   // log2 headroom before the running max is moved
 
@@ -78,9 +78,19 @@ __device__ __forceinline__ void scale_acc(f32x16 &acc, float s) {
     }
 }
 
-template <int SRC>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
+// owns BM = 32 * RB * NW rows of one query head. WPE waves share one SIMD.
+template <int SRC, int NW, int RB, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_mfma_kernel(PrefillArgs a) {
+    constexpr int BM = 32 * RB * NW;
+    constexpr int LPW = 16 / NW;   // 1 KiB direct-load instructions per wave per K (or V) tile
+    static_assert(NW * LPW == 16 && NW >= 2, "waves must split a tile evenly");
+    static_assert(RB == 1 || RB == 2, "row blocks per wave");
+    // Arrays that the lambdas below capture are sized for the largest shape
+    // (RB 2, LPW 8): clang does not emit the host launch stub of a kernel
+    // whose lambdas capture arrays of template-dependent size. Only the
+    // first RB (LPW) entries are ever touched.
     // Two buffers, each a K tile followed by a V tile, 64 keys x 256 bytes each.
     constexpr int kTileBytes = kPfBN * 256;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * kTileBytes];
@@ -93,7 +103,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // blocks and all query heads of that kv head read their K/V tiles through
     // one L2. Within a pair: the last (longest) query blocks first, the
     // group's heads side by side.
-    const int qblocks = (a.max_seqlen_q + kPfBM - 1) / kPfBM;
+    const int qblocks = (a.max_seqlen_q + BM - 1) / BM;
     const int per_pair = qblocks * a.group;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     const int lp = local / per_pair, within = local - lp * per_pair;
@@ -105,19 +115,19 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int h = kvh * a.group + (within - (within / a.group) * a.group);
     const int q_start = a.cu_q[s];
     const int Lq = a.cu_q[s + 1] - q_start;
-    const int q0 = qt * kPfBM;
+    const int q0 = qt * BM;
     if (q0 >= Lq) return;
     const int k_start = a.cu_k[s];
     const int Lk = a.cu_k[s + 1] - k_start;
     const int off = Lk - Lq;
     const int r32 = lane & 31, j = lane >> 5;
-    // The wave owns rows q0 + 64*wave + 32*rb + r32, rb = 0, 1.
+    // The wave owns rows q0 + 32*RB*wave + 32*rb + r32, rb < RB.
     int my_pos[2];
     bool row_ok[2];
     bf16x8 qb[2][8];   // B operand of S^T = K Q^T: Q[row][d = 16*kk + 8*j .. +8]
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int row = q0 + 64 * wave + 32 * rb + r32;
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = q0 + 32 * RB * wave + 32 * rb + r32;
         row_ok[rb] = row < Lq;
         my_pos[rb] = off + row;
         const uint16_t *q = (const uint16_t *)a.q + (int64_t)(q_start + row) * a.q_stride +
@@ -129,34 +139,36 @@ void prefill_mfma_kernel(PrefillArgs a) {
             qb[rb][kk] = __builtin_bit_cast(bf16x8, w);
         }
     }
-    const int kend = min(Lk, off + min(q0 + kPfBM, Lq));   // keys this block needs
+    const int kend = min(Lk, off + min(q0 + BM, Lq));   // keys this block needs
     const int n_kt = (kend + kPfBN - 1) / kPfBN;
-    const int pos_first = off + q0 + 64 * wave;           // position of the wave's first row
+    // Position of the wave's last row: tiles starting past it hold only masked
+    // keys for this wave, which skips their arithmetic (not their loads).
+    const int pos_last = off + q0 + 32 * RB * (wave + 1) - 1;
 
     // Tile loads go global -> LDS directly (buffer_load_dwordx4 ... lds), no
     // registers in between. Instruction i of wave w fills LDS bytes
-    // [1024*(8w+i), +1024) of a tile: keys 4*(8w+i) + lane/16, chunk position
-    // lane%16. Keys at or past kend are outside the descriptor's range and
-    // arrive as zeros.
+    // [1024*(LPW*w+i), +1024) of a tile: keys 4*(LPW*w+i) + lane/16, chunk
+    // position lane%16. Keys at or past kend are outside the descriptor's
+    // range and arrive as zeros.
     const uint8_t *kbase = (const uint8_t *)(SRC == kContiguous ? a.k : a.kc) + (int64_t)kvh * kPfD * 2;
     const uint8_t *vbase = (const uint8_t *)(SRC == kContiguous ? a.v : a.vc) + (int64_t)kvh * kPfD * 2;
     const uint32_t stride_b = (uint32_t)(SRC == kContiguous ? a.kv_stride * 2 : (int64_t)a.Hkv * kPfD * 2);
     const int32_t *bt_row = a.bt + (int64_t)s * a.maxb;
     int voff[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = 4 * (8 * wave + i) + (lane >> 4);
+    for (int i = 0; i < LPW; ++i) {
+        const int t = 4 * (LPW * wave + i) + (lane >> 4);
         const int chunk = (lane & 15) ^ tile_swz(t);
         voff[i] = (SRC == kPoolSmall ? (lane >> 4) : t) * (int)stride_b + 16 * chunk;
     }
     typedef __attribute__((address_space(3))) void lds_t;
     auto load_tile = [&](int k0, uint8_t *dst) {
-        uint8_t *kd = dst + 1024 * 8 * wave;
-        uint8_t *vd = dst + kTileBytes + 1024 * 8 * wave;
+        uint8_t *kd = dst + 1024 * LPW * wave;
+        uint8_t *vd = dst + kTileBytes + 1024 * LPW * wave;
         if constexpr (SRC == kPoolSmall) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int key0 = k0 + 4 * (8 * wave + i);
+            for (int i = 0; i < LPW; ++i) {
+                const int key0 = k0 + 4 * (LPW * wave + i);
                 const int lb = key0 >> a.log2bs;
                 const int blk = (key0 < kend && lb < a.maxb) ? bt_row[lb] : -1;
                 const bool ok = blk >= 0 && blk < a.num_blocks;
@@ -184,7 +196,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + rb_), (short)0, nrec, kBufWord3);
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + rb_), (short)0, nrec, kBufWord3);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < LPW; ++i) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_t *)(kd + 1024 * i), 16, voff[i], 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_t *)(vd + 1024 * i), 16, voff[i], 0, 0, 0);
             }
@@ -210,10 +222,15 @@ void prefill_mfma_kernel(PrefillArgs a) {
             voffr[hi][nt] = t * 256 + 16 * (chunk ^ tile_swz(t)) + 8 * (q16 & 1);
         }
 
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    float m[2], l[2];
     f32x16 o[2][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb) {
+        m[rb] = -INFINITY;
+        l[rb] = 0.f;
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -230,17 +247,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
         if (more) load_tile(k0 + kPfBN, nxt);
         const uint8_t *Ks = cur;
         const uint8_t *Vs = cur + kTileBytes;
-        // No tile is skipped: a tile that lies above some of the wave's rows
-        // (at most the last one of the block) only brings masked scores, which
-        // add nothing, and the wave would wait at the barrier anyway. Keeping
-        // the loop body free of branches around the accumulators keeps them
-        // in place across iterations.
-        {
+        if (!decltype(masked)::value || k0 <= pos_last) {
             // S^T tiles: st[rb][mt][r] = S[row r32 of block rb][key k0 + 32*mt + 8*(r/4) + 4*j + r%4].
             // Every K operand read from LDS feeds both row blocks.
-            f32x16 st[2][2];
+            f32x16 st[RB][2];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -251,16 +263,17 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 for (int kk = 0; kk < 8; ++kk) {
                     const bf16x8 kab = __builtin_bit_cast(bf16x8,
                         *reinterpret_cast<const u32x4 *>(Ks + 32 * 256 * mt + koff[kk]));
-                    st[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kab, qb[0][kk], st[0][mt], 0, 0, 0);
-                    st[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kab, qb[1][kk], st[1][mt], 0, 0, 0);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        st[rb][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kab, qb[rb][kk], st[rb][mt], 0, 0, 0);
                 }
             // Online softmax: causal mask (diagonal tiles only), max on raw
             // scores, one lazy-rescale decision for both row blocks, then
             // p = exp2(q.k * c - m * c) rounded to bf16 and row sums of the
             // rounded p via v_dot2.
-            float mx[2];
+            float mx[RB];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) {
                 if constexpr (decltype(masked)::value) {
                     const int lim = my_pos[rb] - k0 - 4 * j;
 #pragma unroll
@@ -277,9 +290,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
                         x = fmaxf(fmaxf(x, st[rb][mt][r]), st[rb][mt][r + 1]);
                 mx[rb] = xor32_max(x);
             }
-            if (__builtin_amdgcn_ballot_w64(mx[0] * c > m[0] * c + kLazy || mx[1] * c > m[1] * c + kLazy) != 0) {
+            bool grow = false;
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) grow = grow || mx[rb] * c > m[rb] * c + kLazy;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
                     const float m_new = fmaxf(m[rb], mx[rb]);
                     const float alpha = m[rb] == m_new ? 1.f : fast_exp2((m[rb] - m_new) * c);
                     l[rb] *= alpha;
@@ -288,9 +304,9 @@ void prefill_mfma_kernel(PrefillArgs a) {
                     m[rb] = m_new;
                 }
             }
-            bf16x8 pb[2][2][2];   // [rb][mt][ap]
+            bf16x8 pb[RB][2][2];   // [rb][mt][ap]
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) {
                 const float mc = m[rb] * c;
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
@@ -320,8 +336,9 @@ void prefill_mfma_kernel(PrefillArgs a) {
                         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) s16x4 *)(vrow + voffr[1][nt]));
                         const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        o[0][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[0][mt][ap], o[0][nt], 0, 0, 0);
-                        o[1][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[1][mt][ap], o[1][nt], 0, 0, 0);
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb)
+                            o[rb][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[rb][mt][ap], o[rb][nt], 0, 0, 0);
                     }
                 }
         }
@@ -350,11 +367,11 @@ void prefill_mfma_kernel(PrefillArgs a) {
     }
 
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const float lt = xor32_sum(l[rb]);
         if (!row_ok[rb]) continue;
         const float inv = 1.f / lt;
-        const int row = q0 + 64 * wave + 32 * rb + r32;
+        const int row = q0 + 32 * RB * wave + 32 * rb + r32;
         uint16_t *out = (uint16_t *)a.out + ((int64_t)(q_start + row) * a.Hq + h) * kPfD;
         // o[rb][nt][4*g + c] = O[row][d = 32*nt + 8*g + 4*j + c]
 #pragma unroll
@@ -443,16 +460,20 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
     // at least 4 keys; anything else takes the generic kernel.
     const int64_t row_bytes = a.paged ? (int64_t)a.Hkv * a.d * 2 : a.kv_stride * 2;
     if (dtype == 1 && a.d == 128 && (!a.paged || a.bs >= 4) && row_bytes * kPfBN < (1ll << 31)) {
+        // Four waves of 32 query rows per workgroup (one head, 128 rows), two
+        // waves per SIMD: while one wave waits on LDS or runs its softmax the
+        // other keeps the matrix core busy.
+        constexpr int NW = 4, RB = 1, BM = 32 * NW * RB;
         const int64_t pairs = (int64_t)a.num_seqs * a.Hkv;
-        const int64_t nwg = 8 * ((pairs + 7) / 8) * ((a.max_seqlen_q + kPfBM - 1) / kPfBM) * a.group;
+        const int64_t nwg = 8 * ((pairs + 7) / 8) * ((a.max_seqlen_q + BM - 1) / BM) * a.group;
         if (nwg > 0x7fffffff) return hipErrorInvalidValue;
-        const dim3 grid((unsigned)nwg);
+        const dim3 grid((unsigned)nwg), block(64 * NW);
         if (!a.paged)
-            hipLaunchKernelGGL(prefill_mfma_kernel<kContiguous>, grid, dim3(128), 0, stream, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<kContiguous, NW, RB, 2>), grid, block, 0, stream, a);
         else if (a.bs % kPfBN == 0)
-            hipLaunchKernelGGL(prefill_mfma_kernel<kPoolBlocks>, grid, dim3(128), 0, stream, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolBlocks, NW, RB, 2>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL(prefill_mfma_kernel<kPoolSmall>, grid, dim3(128), 0, stream, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2>), grid, block, 0, stream, a);
     } else {
         const dim3 grid((a.max_seqlen_q + 3) / 4, a.Hq, a.num_seqs);
         if (dtype == 0 && a.d == 64)

@@ -253,6 +253,29 @@ def test_balanced_decode_any_wave_count(cuda, waves, monkeypatch):
     assert err <= 2e-2
 
 
+def test_decode_workspace_reuse(cuda):
+    # One caller workspace across calls of different shapes, each call twice:
+    # nothing a call leaves in the workspace may change the next one's result.
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    for seed, lens, hq, hkv in ((1, [900, 33, 2048], 16, 8), (2, [5, 1500], 8, 2),
+                                (3, [900, 33, 2048], 16, 8)):
+        say(f"[gpu] decode workspace reuse, seed {seed}")
+        w = custom_workload(phase="decode", seq_lens=lens, num_cached=[n - 1 for n in lens],
+                            num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=256,
+                            seed=seed)
+        wd = to_device(w, "cuda")
+        kc, vc = alloc_pool(w.num_blocks, 256, hkv, 128, torch.bfloat16, "cuda")
+        write_ranges(w.hist, w.block_tables, 256, wd.k_hist, wd.v_hist, kc, vc)
+        meta = pkv.pack_decode(w.seq_lens, w.block_tables, 256)
+        pkv.store_kvcache(wd.k_new, wd.v_new, kc, vc, meta["slot_mapping"])
+        for rep in range(2):
+            out = pkv.decode_attention_paged(wd.q, kc, vc, meta["block_tables"], meta["context_lens"],
+                                             meta["max_seqlen_k"], w.scale, workspace=ws)
+            torch.cuda.synchronize()
+            want, *_ = oracle.run_workload(w)
+            assert max_abs_err(out, want) <= 2e-2
+
+
 def test_balanced_decode_padded_rows(cuda):
     say("[gpu] balanced decode with padding rows (context 0) between real ones")
     w = custom_workload(phase="decode", seq_lens=[300, 1000], num_cached=[299, 999], num_q_heads=8,
