@@ -355,6 +355,10 @@ def summarize_counters(fetch_dir, write_dir, workload):
 
 # ----------------------------------------------------------------- main
 
+# Steps per chunk of the event-timed pass (see the comment there).
+EVENT_CHUNK_STEPS = 10
+
+
 def preroll_cycles(seconds: float) -> int:
     """Argument of torch.cuda._sleep that keeps the GPU busy for about
     `seconds` (calibrated once with events), capped at 0.5 s."""
@@ -438,6 +442,10 @@ def main():
     # The same steps again, each call bracketed by HIP events on its stream.
     # The host enqueues them while a short spin kernel holds the GPU, so the
     # kernels run back to back and no interval contains host launch latency.
+    # The pass goes in chunks of a few steps, each behind its own spin and
+    # followed by a synchronize: with hundreds of commands outstanding the
+    # runtime makes the host wait for queue space, and the GPU would then
+    # idle inside the timed intervals.
     for p in parts:
         p.prepare(args.steps)
     events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in parts]
@@ -449,17 +457,26 @@ def main():
             for e in evs:
                 e.record()
     torch.cuda.synchronize()
-    preroll_s = 4 * t_host + 10e-3
-    torch.cuda._sleep(preroll_cycles(preroll_s))
-    t_enq = time.perf_counter()
-    keep = [p.run(i, events[i][parts.index(p)]) for (i, p) in order(0)]
-    t_enq = time.perf_counter() - t_enq
-    torch.cuda.synchronize()
-    del keep
-    gpu_span = events[0][0][0].elapsed_time(events[-1][-1][3]) * 1e-3
+    chunk = EVENT_CHUNK_STEPS
+    preroll_s = 4 * t_host * chunk / args.steps + 5e-3
+    cycles = preroll_cycles(preroll_s)
+    t_enq_max, late = 0.0, 0
+    for p in parts:
+        for c0 in range(0, args.steps, chunk):
+            torch.cuda._sleep(cycles)
+            t_enq = time.perf_counter()
+            keep = [p.run(i, events[i][parts.index(p)]) for i in range(c0, min(c0 + chunk, args.steps))]
+            t_enq = time.perf_counter() - t_enq
+            torch.cuda.synchronize()
+            del keep
+            t_enq_max = max(t_enq_max, t_enq)
+            late += t_enq > preroll_s
+    if late:
+        log(f"[bench] WARNING: in {late} chunk(s) the host enqueue outlasted the pre-roll; "
+            "those intervals may hold host gaps")
     log(f"[bench] wall {wall * 1e3:.2f} ms for {args.steps} steps (host {t_host * 1e3:.1f} ms); "
-        f"event pass: host enqueue {t_enq * 1e3:.1f} ms behind a {preroll_s * 1e3:.0f} ms pre-roll, "
-        f"gpu span {gpu_span * 1e3:.2f} ms")
+        f"event pass in chunks of {chunk} steps: longest host enqueue {t_enq_max * 1e3:.2f} ms "
+        f"behind a {preroll_s * 1e3:.1f} ms pre-roll")
     for j, p in enumerate(parts):
         p.collect([events[i][j] for i in range(args.steps)])
     summaries = [p.summary() for p in parts]
@@ -503,6 +520,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": config, "roofline": roof, "cpu_baseline": cpu_main,
         "secondary": {}, "parts": summaries, "cpu_baselines": cpu,
+        "event_timing": {"chunk_steps": EVENT_CHUNK_STEPS, "chunks_with_host_gaps": late},
     }
     if pre is not None:
         line["secondary"]["prefill_attention_TFLOPs"] = pre["attention_TFLOPs"]
