@@ -64,20 +64,6 @@ enum KeySource {
 // has LDS bank conflicts.
 __device__ __forceinline__ int tile_swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
 
-// acc *= s in place, element by element through one VGPR. Written with AGPR
-// operands so that the output accumulators stay in the accumulation registers
-// across the key loop (a plain multiply would make the compiler copy all of
-// them out to VGPRs and back on every tile, for a rescale that rarely runs).
-__device__ __forceinline__ void scale_acc(f32x16 &acc, float s) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        float x = acc[r], t;
-        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                     : "+a"(x), "=&v"(t) : "v"(s));
-        acc[r] = x;
-    }
-}
-
 // NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
 // owns BM = 32 * RB * NW rows of one query head. WPE waves share one SIMD.
 template <int SRC, int NW, int RB, int WPE>
@@ -299,8 +285,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
                     const float m_new = fmaxf(m[rb], mx[rb]);
                     const float alpha = m[rb] == m_new ? 1.f : fast_exp2((m[rb] - m_new) * c);
                     l[rb] *= alpha;
+                    // A plain multiply: the compiler then keeps every
+                    // accumulator in ordinary VGPRs (206 of them, no AGPRs,
+                    // nothing spilled), so the scores need no copies out of
+                    // the accumulation registers either.
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) scale_acc(o[rb][nt], alpha);
+                    for (int nt = 0; nt < 4; ++nt) o[rb][nt] *= alpha;
                     m[rb] = m_new;
                 }
             }
