@@ -49,6 +49,10 @@ WORKLOADS = {
     "prefill": [("prefill", 3)],
     "decode-long": [("decode", 5)],
     "prefill-prefix": [("prefill", 4)],
+    # decode rows through the varlen prefill call, beside the decode kernel on
+    # the same batch; and a mixed step (decode rows + two prompt chunks)
+    "decode-in-varlen": [("decode", 2), ("prefill", 6)],
+    "mixed": [("prefill", 7)],
 }
 
 
@@ -67,6 +71,18 @@ def decode_bytes(w) -> float:
     kv = int(ctx.sum()) * 2 * w.num_kv_heads * w.head_dim * es
     qo = 2 * len(ctx) * w.num_q_heads * w.head_dim * es
     meta = int(np.sum(-(-ctx // w.block_size))) * 4 + len(ctx) * 4
+    return float(kv + qo + meta)
+
+
+def prefill_bytes(w) -> float:
+    """Algorithmic bytes of one prefill attention call: every key position's K
+    and V row of every kv head read once, q read and out written once, plus
+    the cu_seqlens and (paged) the block-table entries in use."""
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    lk = np.asarray(w.seq_lens, dtype=np.int64)
+    kv = int(lk.sum()) * 2 * w.num_kv_heads * w.head_dim * es
+    qo = 2 * w.total_q * w.num_q_heads * w.head_dim * es
+    meta = 2 * (len(lk) + 1) * 4 + int(np.sum(-(-lk // w.block_size))) * 4
     return float(kv + qo + meta)
 
 
@@ -191,8 +207,11 @@ class Part:
                       "partition_size": self.partition})
         else:
             f = prefill_flops(w)
+            b = prefill_bytes(w)
             d.update({"attention_flops": f, "attention_TFLOPs": f / t_attn / 1e12,
-                      "attention_frac_mfma": f / t_attn / 1e12 / MFMA_BF16_PEAK_TFLOPS})
+                      "attention_frac_mfma": f / t_attn / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                      "attention_bytes": b, "attention_GBps": b / t_attn / 1e9,
+                      "attention_frac_hbm": b / t_attn / 1e9 / HBM_PEAK_GBS})
         return d
 
 
@@ -235,7 +254,9 @@ def cpu_baseline(phase, preset, budget_s):
                           f"oracle store + decode attention, {reps} repetition(s), {t:.1f} s",
                 "cpu": cpu}
     # prefill: one sequence per oracle call, cycling over the front of the batch
-    t, flops, calls, seen = 0.0, 0.0, 0, set()
+    # (rate in GB/s for a batch below the ridge point, as for the GPU figure)
+    byte_bound = prefill_flops(shape) / prefill_bytes(shape) < MFMA_BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS
+    t, flops, nbytes, calls, seen = 0.0, 0.0, 0.0, 0, set()
     s = 0
     while t < budget_s:
         w = restrict(shape, [s])
@@ -253,10 +274,12 @@ def cpu_baseline(phase, preset, budget_s):
                              k=w.k_new, v=w.v_new)
         t += time.perf_counter() - t0
         flops += prefill_flops(w)
+        nbytes += prefill_bytes(w)
         calls += 1
         seen.add(s)
         s = (s + 1) % len(shape.seq_lens)
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    value, unit = (nbytes / t / 1e9, "GB/s") if byte_bound else (flops / t / 1e12, "TFLOP/s")
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"{calls} oracle prefill calls, one sequence each, over {len(seen)} of the "
                       f"preset's {len(shape.seq_lens)} sequences (store + attention through the "
                       f"block tables where the preset reads the cache), {t:.1f} s",
@@ -501,7 +524,7 @@ def main():
                           + " (one decode_attention_paged call)",
                 "algorithmic_bytes_per_launch": per_launch, "avg_launch_us": dec["attention_us"]}
         cpu_main = cpu.get("decode")
-    else:
+    elif pre["attention_flops"] / pre["attention_bytes"] >= MFMA_BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS:
         value, unit = pre["attention_TFLOPs"], "TFLOP/s"
         roof = {"bound": "mfma", "achieved": value, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": value / MFMA_BF16_PEAK_TFLOPS,
@@ -509,8 +532,19 @@ def main():
                 "kernel": "prefill_mfma_kernel", "algorithmic_flops_per_launch": pre["attention_flops"],
                 "avg_launch_us": pre["attention_us"]}
         cpu_main = cpu.get("prefill")
+    else:
+        # a prefill call below the ridge point (decode rows, short chunks over
+        # long cached contexts) is bound by its K/V bytes
+        value, unit = pre["attention_GBps"], "GB/s"
+        roof = {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": value / HBM_PEAK_GBS,
+                "traffic": counters_traffic("prefill.hip", f"prefill-preset{pre['preset']}"),
+                "kernel": "prefill_mfma_kernel", "algorithmic_bytes_per_launch": pre["attention_bytes"],
+                "avg_launch_us": pre["attention_us"]}
+        cpu_main = cpu.get("prefill")
     names = {2: "decode-qwen3-0.6b-b64-ctx512-4096", 3: "prefill-varlen-16x-u128-2048-budget16384",
-             4: "prefill-prefix-hit-32x2048", 5: "decode-qwen3-8b-b512-ctx256-32768"}
+             4: "prefill-prefix-hit-32x2048", 5: "decode-qwen3-8b-b512-ctx256-32768",
+             6: "decode-in-varlen-qwen3-0.6b-b64", 7: "mixed-b64-decode+2x512-chunks"}
     config = {"workload": " + ".join(names[p.preset] for p in parts),
               "parts": [{"phase": p.phase, **p.w.describe()} for p in parts],
               "copies_in_rotation": [len(p.copies) for p in parts]}

@@ -86,7 +86,7 @@ def test_decode_packer_matches_oracle_and_pages():
 
 
 def test_packers_on_presets():
-    for k in (1, 2, 3, 4, 5):
+    for k in (1, 2, 3, 4, 5, 6, 7):
         w = make_workload(k, values=False)
         if w.phase == "decode":
             m = pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cpu")

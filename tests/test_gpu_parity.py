@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the oracle on the same
 seeded inputs. store_kvcache is compared bit for bit over the pool; attention
 within max |err| 2e-2 for bf16 inputs (fp32 accumulation) and 1e-4 for fp32.
-Presets 1-3 are checked in full; presets 4 and 5 (the largest) run at full
-size on the GPU and are checked on sampled sequences the oracle computes."""
+Presets 1-3, 6 and 7 are checked in full; presets 4 and 5 (the largest) run
+at full size on the GPU and are checked on sampled sequences the oracle
+computes."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
 
-FULL = [(1, "prefill"), (1, "decode"), (2, None), (3, None)]
+FULL = [(1, "prefill"), (1, "decode"), (2, None), (3, None), (6, None), (7, None)]
 
 
 def _ids(p):
@@ -295,3 +296,40 @@ def test_balanced_decode_padded_rows(cuda):
     want, *_ = oracle.run_workload(w)
     assert max_abs_err(out[[0, 2]], want) <= 2e-2
     assert torch.count_nonzero(out[[1, 3]].float()) == 0
+
+
+MIXED = [
+    # (seq_lens, num_cached, block_size): decode rows (Lq = 1), prompt chunks
+    # whose cache boundary falls inside a block, a fresh prompt and a
+    # one-token fresh prompt, all in one varlen call
+    ([300, 129, 1, 77, 515, 64], [299, 100, 0, 76, 256, 0], 16),
+    ([300, 129, 1, 77, 515, 64], [299, 100, 0, 76, 256, 0], 256),
+    ([2049, 1000, 4096], [2048, 999, 3000], 64),
+]
+
+
+@pytest.mark.parametrize("case", MIXED, ids=lambda c: f"bs{c[2]}-{len(c[0])}seqs")
+def test_mixed_batch(cuda, case):
+    lens, cached, bs = case
+    say(f"[gpu] mixed varlen batch {case}")
+    w = custom_workload(phase="prefill", seq_lens=lens, num_cached=cached, num_q_heads=16,
+                        num_kv_heads=8, head_dim=128, block_size=bs, seed=sum(lens) + bs)
+    out, kc, vc = gpu_run(to_device(w, "cuda"))
+    want, kp, vp, _ = oracle.run_workload(w)
+    assert np.array_equal(raw(kc), raw(kp)) and np.array_equal(raw(vc), raw(vp))
+    err = max_abs_err(out, want)
+    say(f"  max |err| = {err:.3e}")
+    assert err <= 2e-2
+
+
+def test_decode_in_varlen_matches_decode_kernel(cuda):
+    say("[gpu] preset 6 (preset 2's batch as Lq = 1 varlen rows) vs the decode kernel")
+    w = make_workload(6)
+    out_v, *_ = gpu_run(to_device(w, "cuda"))
+    w.phase = "decode"
+    out_d, *_ = gpu_run(to_device(w, "cuda"))
+    want, *_ = oracle.run_workload(w)
+    assert max_abs_err(out_v, want) <= 2e-2 and max_abs_err(out_d, want) <= 2e-2
+    d = (out_v.float() - out_d.float()).abs().max().item()
+    say(f"  varlen vs decode kernel max |diff| = {d:.3e}")
+    assert d <= 2e-2

@@ -311,6 +311,35 @@ def test_decode_equals_last_prefill_row():
         np.testing.assert_allclose(dec[s], full[n - 1], rtol=0, atol=1e-12)
 
 
+def test_mixed_batch_rows_equal_decode_and_full_recompute():
+    # A chunked-prefill step mixes, in one varlen call, sequences with Lq = 1
+    # (decode), Lq < Lk with a cache boundary inside a block (a prompt chunk)
+    # and Lq = Lk (a fresh prompt). Bottom-right alignment makes each row the
+    # row of the same position in a full recomputation of its sequence, and an
+    # Lq = 1 row the decode result for that sequence.
+    lens, cached = [45, 70, 30, 17], [44, 50, 0, 16]
+    kw = dict(num_q_heads=4, num_kv_heads=2, head_dim=16, block_size=16,
+              dtype=torch.float32, seed=21)
+    mixed = custom_workload(phase="prefill", seq_lens=lens, num_cached=cached, **kw)
+    got, *_ = oracle.run_workload(mixed)
+    kv = logical_kv(mixed)
+    qo = np.concatenate([[0], np.cumsum([n - c for n, c in zip(lens, cached)])])
+    for s, (n, c) in enumerate(zip(lens, cached)):
+        k, v = kv[s]
+        q = torch.zeros(n, 4, 16)
+        q[c:] = mixed.q[qo[s]:qo[s + 1]]
+        full = oracle.attention(q, [n], [n], 2, mixed.scale,
+                                k=torch.tensor(k, dtype=torch.float32),
+                                v=torch.tensor(v, dtype=torch.float32))
+        np.testing.assert_allclose(got[qo[s]:qo[s + 1]], full[c:], rtol=0, atol=1e-12)
+    # the Lq = 1 rows against the decode phase on the same cache and queries
+    dec = custom_workload(phase="decode", seq_lens=[45, 17], num_cached=[44, 16], **kw)
+    dec_pre = custom_workload(phase="prefill", seq_lens=[45, 17], num_cached=[44, 16], **kw)
+    a, *_ = oracle.run_workload(dec)
+    b, *_ = oracle.run_workload(dec_pre)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
 def test_gqa_equals_mha_with_repeated_kv_heads():
     w = custom_workload(phase="prefill", seq_lens=[23, 9], num_cached=[0, 0], num_q_heads=6,
                         num_kv_heads=2, head_dim=8, block_size=4, dtype=torch.float32, seed=14,
@@ -389,6 +418,13 @@ def test_presets_shapes():
     assert len(w5.seq_lens) == 512 and min(w5.seq_lens) >= 256 and max(w5.seq_lens) <= 32768
     used = sum(w5.block_tables, [])
     assert len(used) == w5.num_blocks == len(set(used))
+    w6 = make_workload(6, values=False)
+    assert w6.phase == "prefill" and w6.seq_lens == w2.seq_lens and w6.block_tables == w2.block_tables
+    assert w6.total_q == 64 and all(n - c == 1 for n, c in zip(w6.seq_lens, w6.num_cached))
+    w7 = make_workload(7, values=False)
+    assert w7.total_q == 64 + 2 * 512 and w7.num_cached[-2:] == [1536, 1536]
+    used = sum(w7.block_tables, [])
+    assert len(used) == len(set(used)) and max(used) < w7.num_blocks
 
 
 def test_bf16_rounding_is_round_to_nearest_even():

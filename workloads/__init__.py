@@ -218,18 +218,46 @@ def _preset5(rng, phase):
     return _decode_batch(rng, 512, 256, 32768, True, 256, 32, 8, pool=None)
 
 
+def _preset6(rng, phase):
+    # Decode through the varlen prefill call: preset 2's batch (the same context
+    # lengths and block tables, drawn from preset 2's seed) as one prefill step
+    # whose every sequence has all but its newest token cached (Lq = 1).
+    spec = _decode_batch(np.random.default_rng(1002), 64, 512, 4096, False, 256, 16, 8, pool=2048)
+    return dict(spec, phase="prefill")
+
+
+def _preset7(rng, phase):
+    # A mixed (chunked-prefill) step: preset 2's kind of decode batch -- 64
+    # sequences, context U{512..4096}, Lq = 1 -- plus two prompts of 2048 tokens
+    # whose first 1536 are cached, each contributing a 512-token chunk, in one
+    # varlen call. The chunks' blocks follow the decode pool.
+    spec = _decode_batch(rng, 64, 512, 4096, False, 256, 16, 8, pool=2048)
+    bs, n, c = 256, 2048, 1536
+    pool = spec["num_blocks"]
+    for i in range(2):
+        s = len(spec["seq_lens"])
+        spec["block_tables"].append(list(range(pool + i * (n // bs), pool + (i + 1) * (n // bs))))
+        spec["seq_lens"].append(n)
+        spec["num_cached"].append(c)
+        spec["hist"].append((s, 0, c))
+    spec["num_blocks"] = pool + 2 * (n // bs)
+    return dict(spec, phase="prefill")
+
+
 PRESETS = {
     1: ("tiny-fp32-paged", _preset1),
     2: ("decode-qwen3-0.6b-b64", _preset2),
     3: ("prefill-varlen-16x-u128-2048", _preset3),
     4: ("prefill-prefix-hit-32x2048", _preset4),
     5: ("decode-qwen3-8b-b512-long", _preset5),
+    6: ("decode-in-varlen-qwen3-0.6b-b64", _preset6),
+    7: ("mixed-b64-decode+2x512-chunks", _preset7),
 }
 
 
 def make_workload(preset: int, phase: Optional[str] = None, device: str = "cpu",
                   values: bool = True) -> Workload:
-    """Build preset ``preset`` (1..5). Preset 1 has both phases: ``phase`` picks
+    """Build preset ``preset`` (1..7). Preset 1 has both phases: ``phase`` picks
     "prefill" (default) or "decode". ``values=False`` skips drawing tensors."""
     name, fn = PRESETS[preset]
     seed = 1000 + preset
