@@ -53,6 +53,8 @@ WORKLOADS = {
     # the same batch; and a mixed step (decode rows + two prompt chunks)
     "decode-in-varlen": [("decode", 2), ("prefill", 6)],
     "mixed": [("prefill", 7)],
+    # preset 3's step with the rotary embedding fused into the store
+    "rope-store": [("prefill+rope", 3)],
 }
 
 
@@ -72,6 +74,21 @@ def decode_bytes(w) -> float:
     qo = 2 * len(ctx) * w.num_q_heads * w.head_dim * es
     meta = int(np.sum(-(-ctx // w.block_size))) * 4 + len(ctx) * 4
     return float(kv + qo + meta)
+
+
+ROPE_BASE, ROPE_MAX_POS = 1e6, 40960
+
+
+def rope_store_bytes(w) -> float:
+    """Fused rotary embedding + store, per token: q read and written, k read
+    and written to the cache (and back in place when the step's prefill reads
+    k directly), v read and written, the slot and the position, and one
+    position's cos/sin row (head_dim floats)."""
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    q = 2 * w.num_q_heads * w.head_dim * es
+    kv = w.num_kv_heads * w.head_dim * es
+    k = kv * (3 if not w.use_block_tables else 2)
+    return float(w.total_q * (q + k + 2 * kv + 8 + 4 * w.head_dim))
 
 
 def prefill_bytes(w) -> float:
@@ -112,6 +129,9 @@ class Part:
         from paged_kv_cache_125_amd.step import alloc_pool, step_inputs_of, write_ranges
         from workloads import make_workload
         self.pkv = pkv
+        # "prefill+rope": the store is the fused rotary embedding + store
+        self.rope = phase.endswith("+rope")
+        phase = phase.split("+")[0]
         self.phase, self.preset = phase, preset
         self.copies = []
         w = None
@@ -131,6 +151,10 @@ class Part:
             self.partition = pkv.decode_partition_size(len(w.seq_lens), max(w.seq_lens),
                                                        w.num_q_heads, w.num_kv_heads, w.head_dim,
                                                        w.block_size, w.dtype)
+        if self.rope:
+            # Qwen3's rotary embedding: the whole head rotated, base 1e6,
+            # "rotate half" pairing, positions up to 40960
+            self.cos_sin = pkv.rope_cos_sin_table(ROPE_MAX_POS, w.head_dim, ROPE_BASE, device="cuda")
         self.names = ["pack", "store", "attention"]
         self.times = {n: [] for n in self.names}
         self.ring = []
@@ -168,7 +192,12 @@ class Part:
             meta = pkv.pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size,
                                     host_buffer=hb, dev_buffer=db)
             rec(1)
-            pkv.store_kvcache(w.k_new, w.v_new, kc, vc, meta["slot_mapping"])
+            if self.rope:
+                pkv.rope_store_kvcache(w.q, w.k_new, w.v_new, kc, vc, meta["slot_mapping"],
+                                       meta["positions"], self.cos_sin,
+                                       write_k=meta["block_tables"] is None)
+            else:
+                pkv.store_kvcache(w.k_new, w.v_new, kc, vc, meta["slot_mapping"])
             rec(2)
             if meta["block_tables"] is not None:
                 pkv.prefill_attention_varlen(w.q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
@@ -192,8 +221,9 @@ class Part:
         t_attn = float(np.mean(self.times["attention"]))
         t_store = float(np.mean(self.times["store"]))
         t_pack = float(np.mean(self.times["pack"]))
-        sb = store_bytes(w)
-        d = {"workload": w.name, "preset": self.preset, "phase": self.phase,
+        sb = rope_store_bytes(w) if self.rope else store_bytes(w)
+        d = {"workload": w.name + ("+rope" if self.rope else ""), "preset": self.preset,
+             "phase": self.phase, "store": "rope_store_kvcache" if self.rope else "store_kvcache",
              "num_seqs": len(w.seq_lens), "tokens_q": w.total_q,
              "context_tokens": int(sum(w.seq_lens)),
              "pack_us": t_pack * 1e6, "store_us": t_store * 1e6, "attention_us": t_attn * 1e6,

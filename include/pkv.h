@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
     PKV_OK = 0,
@@ -190,6 +190,56 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len,
                                   int32_t partition_size);
 
 /* ---------------------------------------------------------------------------
+ * Rotary embedding fused with store_kvcache (the step just before the KV write
+ * in the attention layer: "Nano vLLM 解读（5）：解析 ModelRunner", the attention
+ * layer's forward, and "nano-vLLM-1", "4. prefill 输入打包", where positions are
+ * packed for it). The pages name RoPE but give neither its base nor its
+ * variant, so both are parameters; the rotation itself is that of RoFormer
+ * (Su et al., 2021): pair j of a head vector at position p turns by the angle
+ *     theta_j(p) = p * base^(-2j / rot_dim),   j in [0, rot_dim / 2),
+ *     (x, y) -> (x cos theta - y sin theta,  y cos theta + x sin theta).
+ * style PKV_ROPE_HALF pairs elements (j, j + rot_dim/2) (the "rotate half"
+ * layout of GPT-NeoX / Llama / Qwen); PKV_ROPE_INTERLEAVED pairs (2j, 2j+1)
+ * (GPT-J). Elements at or past rot_dim are not rotated.
+ *
+ * pkv_rope_cos_sin_table fills, on the host (no GPU involved), the float table
+ *     cos_sin[p * rot_dim + j]               = cos(theta_j(p))
+ *     cos_sin[p * rot_dim + rot_dim / 2 + j] = sin(theta_j(p))
+ * for p in [0, max_positions), computed in double and rounded to float. The
+ * caller copies it to the device once (it depends only on the model).
+ * Errors: PKV_EINVAL for a null pointer, max_positions < 1, rot_dim odd or
+ * < 2, or base <= 0.
+ *
+ * pkv_rope_store_kvcache, for each token i in [0, num_tokens) with
+ * p = positions[i] (device int32, 0 <= p < max_positions; a position outside
+ * that range is clamped into it):
+ *   - rotates q[i, h, :rot_dim] in place for every q head h;
+ *   - rotates k row i, writes it to k_cache row slot_mapping[i] (skipped when
+ *     the slot is negative or past the pool, as in pkv_store_kvcache) and, if
+ *     write_k != 0, back into k in place (needed when the same step's prefill
+ *     reads k/v directly rather than through the block tables);
+ *   - copies v row i bit for bit to v_cache row slot_mapping[i].
+ * Arithmetic in float with fused multiply-adds; results round to nearest even
+ * in the storage dtype. Layouts as in pkv_store_kvcache, with q
+ * [num_tokens, num_q_heads, head_dim] at token stride q_token_stride; cos_sin
+ * is the device copy of the table above. Requires rot_dim even, <= head_dim,
+ * and a multiple of 16 / element_size (2 * 16 / element_size for
+ * PKV_ROPE_HALF), rows and strides multiples of 16 bytes, pointers 16-byte
+ * aligned. num_tokens == 0 is a no-op. k and the caches must not overlap q.
+ * -------------------------------------------------------------------------*/
+typedef enum { PKV_ROPE_HALF = 0, PKV_ROPE_INTERLEAVED = 1 } pkv_rope_style;
+
+int pkv_rope_cos_sin_table(float *host_out, int32_t max_positions, int32_t rot_dim, double base);
+
+int pkv_rope_store_kvcache(void *q, int64_t q_token_stride, void *k, const void *v,
+                           int64_t k_token_stride, int64_t v_token_stride, void *k_cache,
+                           void *v_cache, const int32_t *slot_mapping, const int32_t *positions,
+                           const float *cos_sin, int32_t max_positions, int32_t rot_dim,
+                           int32_t style, int32_t write_k, int32_t num_tokens,
+                           int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Host metadata packing ([NV1] "4. prefill 输入打包" and "5. deocde 输入打包":
  * prepare_block_tables, prepare_prefill, prepare_decode; pinned memory and
  * one asynchronous host-to-device copy.)
@@ -211,10 +261,14 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len,
  *   cu_seqlens_k   int32 [num_seqs+1]  prefix sums of seq_lens
  *   block_tables   int32 [num_seqs, max_blocks_per_seq], -1 padded, present
  *                  only when the batch has a cached prefix (total_k > total_q)
+ *   positions      int32 [num_slots]   the positions themselves, same order
+ *                  ([NV1] "4. prefill 输入打包": positions start at
+ *                  num_cached_tokens; they drive the rotary embedding)
  * Decode packs:
  *   slot_mapping   int32 [num_seqs]    slot of position seq_lens[s] - 1
  *   context_lens   int32 [num_seqs]    seq_lens[s]
  *   block_tables   int32 [num_seqs, max_blocks_per_seq], -1 padded (always)
+ *   positions      int32 [num_seqs]    seq_lens[s] - 1
  * Errors: PKV_EINVAL if a sequence's table has fewer than ceil(len / bs)
  * entries, a length is negative (prefill) or < 1 (decode), num_cached exceeds
  * len, or a count overflows int32; PKV_ENOSPACE if the buffer is too small. */
@@ -233,6 +287,7 @@ typedef struct {
     int64_t off_cu_seqlens_k;
     int64_t off_context_lens;
     int64_t off_block_tables;
+    int64_t off_positions;
     int64_t total_bytes;
 } pkv_batch_layout;
 

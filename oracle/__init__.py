@@ -58,6 +58,8 @@ def lib():
         L.orc_attention.restype = ctypes.c_int
         L.orc_attention.argtypes = [i32, P, P, P, i32, i32, i32, dbl, ctypes.c_int,
                                     ctypes.c_int, P, P, P, P, P, P, i32, i64, P, ctypes.c_int]
+        L.orc_rope.restype = ctypes.c_int
+        L.orc_rope.argtypes = [P, i64, i32, i32, P, i32, dbl, i32]
         L.orc_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -97,6 +99,27 @@ def as_storage(x) -> Tuple[np.ndarray, int]:
     if x.dtype == np.float32:
         return x, F32
     raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+def to_f64(x) -> np.ndarray:
+    """The exact float64 values of a bf16 / fp32 tensor or array."""
+    s, code = as_storage(x)
+    if code == BF16:
+        return (s.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return s.astype(np.float64)
+
+
+def rope(x, positions, rot_dim: int, base: float, style: int = 0) -> np.ndarray:
+    """Rotary position embedding of head vectors x [T, H, d] at int positions
+    [T] (``orc_rope``: pair j turns by positions[t] * base**(-2j/rot_dim);
+    style 0 pairs (j, j + rot_dim/2), style 1 pairs (2j, 2j+1)). fp64 result."""
+    v = np.ascontiguousarray(to_f64(x))
+    T, H, d = v.shape
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    assert pos.shape == (T,)
+    if lib().orc_rope(_ptr(v), T, H, d, _ptr(pos), int(rot_dim), float(base), int(style)) != 0:
+        raise ValueError("bad rotary arguments")
+    return v
 
 
 def slot(table: Sequence[int], block_size: int, pos: int) -> int:

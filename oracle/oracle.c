@@ -266,6 +266,37 @@ int orc_attention(int32_t num_seqs, const int32_t *q_lens, const int32_t *k_lens
     return err;
 }
 
+/* Rotary position embedding, in place on fp64 head vectors x [T, H, d]
+ * (row t, head h at x + (t * H + h) * d). The pages name the positions that
+ * feed it ([NV1] "4. prefill 输入打包": positions start at
+ * num_cached_tokens) but not the rotation; this is RoFormer's (Su et al.,
+ * 2021, section 3.2 and its equation for the general case): pair j of the
+ * vector at position p, j in [0, rot_dim / 2), turns by the angle
+ *     theta_j = p * base^(-2j / rot_dim)
+ * as the 2-D rotation (a, b) -> (a cos theta - b sin theta, b cos theta + a sin theta).
+ * style 0 pairs elements (j, j + rot_dim / 2); style 1 pairs (2j, 2j + 1).
+ * Elements at or past rot_dim are left alone. Returns 0, or -1 on bad arguments. */
+int orc_rope(double *x, int64_t T, int32_t H, int32_t d, const int32_t *pos, int32_t rot_dim,
+             double base, int32_t style) {
+    if (rot_dim < 2 || rot_dim % 2 || rot_dim > d || !(base > 0.0) || (style != 0 && style != 1))
+        return -1;
+    const int32_t half = rot_dim / 2;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t h = 0; h < H; ++h) {
+            double *v = x + (t * H + h) * (int64_t)d;
+            for (int32_t j = 0; j < half; ++j) {
+                const double theta = (double)pos[t] * pow(base, -2.0 * j / rot_dim);
+                const double c = cos(theta), sn = sin(theta);
+                const int32_t ia = style == 0 ? j : 2 * j;
+                const int32_t ib = style == 0 ? j + half : 2 * j + 1;
+                const double a = v[ia], b = v[ib];
+                v[ia] = a * c - b * sn;
+                v[ib] = b * c + a * sn;
+            }
+        }
+    return 0;
+}
+
 int orc_max_threads(void)
 {
 #ifdef _OPENMP

@@ -21,7 +21,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpkv.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 PKV_F32, PKV_BF16 = 0, 1
 _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_ELAUNCH", 4: "PKV_ENOSPACE"}
@@ -30,6 +30,7 @@ EXPORTED = [
     "pkv_abi_version", "pkv_last_error", "pkv_store_kvcache", "pkv_prefill_attention_varlen",
     "pkv_decode_attention_paged", "pkv_decode_partition_size", "pkv_decode_workspace_bytes",
     "pkv_plan_prefill", "pkv_pack_prefill", "pkv_plan_decode", "pkv_pack_decode", "pkv_upload",
+    "pkv_rope_cos_sin_table", "pkv_rope_store_kvcache",
 ]
 
 
@@ -47,7 +48,8 @@ class BatchLayout(ctypes.Structure):
         ("num_slots", ctypes.c_int32), ("is_prefill", ctypes.c_int32),
         ("off_slot_mapping", ctypes.c_int64), ("off_cu_seqlens_q", ctypes.c_int64),
         ("off_cu_seqlens_k", ctypes.c_int64), ("off_context_lens", ctypes.c_int64),
-        ("off_block_tables", ctypes.c_int64), ("total_bytes", ctypes.c_int64),
+        ("off_block_tables", ctypes.c_int64), ("off_positions", ctypes.c_int64),
+        ("total_bytes", ctypes.c_int64),
     ]
 
 
@@ -88,6 +90,11 @@ def lib():
     L.pkv_pack_decode.argtypes = [i32, P, P, P, i32, ctypes.POINTER(BatchLayout), P, sz]
     L.pkv_upload.restype = ctypes.c_int
     L.pkv_upload.argtypes = [P, P, sz, P]
+    L.pkv_rope_cos_sin_table.restype = ctypes.c_int
+    L.pkv_rope_cos_sin_table.argtypes = [P, i32, i32, ctypes.c_double]
+    L.pkv_rope_store_kvcache.restype = ctypes.c_int
+    L.pkv_rope_store_kvcache.argtypes = [P, i64, P, P, i64, i64, P, P, P, P, P, i32, i32, i32, i32,
+                                         i32, i32, i32, i32, i32, i32, i32, P]
     if L.pkv_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libpkv ABI {L.pkv_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = L
@@ -134,6 +141,41 @@ def store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cac
                                    _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
                                    int(slot_mapping.numel()), nb, bs, hkv, d, _dtype_code(k_cache),
                                    _stream(stream)))
+
+
+ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+
+
+def rope_cos_sin_table(max_positions: int, rot_dim: int, base: float,
+                       device="cuda") -> torch.Tensor:
+    """pkv_rope_cos_sin_table: float [max_positions, rot_dim] (cos | sin),
+    filled on the host and copied to ``device``."""
+    t = torch.empty((max_positions, rot_dim), dtype=torch.float32)
+    _check(lib().pkv_rope_cos_sin_table(ctypes.c_void_p(t.data_ptr()), int(max_positions),
+                                        int(rot_dim), float(base)))
+    return t.to(device)
+
+
+def rope_store_kvcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, slot_mapping: torch.Tensor, positions: torch.Tensor,
+                       cos_sin: torch.Tensor, style: int = ROPE_HALF, write_k: bool = True,
+                       stream=None) -> None:
+    """pkv_rope_store_kvcache: rotate q (in place) and k by ``positions``,
+    store the rotated k and v into the caches at ``slot_mapping`` (and the
+    rotated k back into ``k`` when ``write_k``)."""
+    nb, bs, hkv, d = k_cache.shape
+    n, hq, _ = q.shape
+    if slot_mapping.dtype != torch.int32 or positions.dtype != torch.int32:
+        raise TypeError("slot_mapping and positions must be int32")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or not cos_sin.is_contiguous():
+        raise TypeError("cos_sin must be a contiguous float32 [max_positions, rot_dim] table")
+    if slot_mapping.numel() != n or positions.numel() != n or k.shape[0] != n or v.shape[0] != n:
+        raise ValueError("q, k, v, slot_mapping and positions must have one entry per token")
+    _check(lib().pkv_rope_store_kvcache(
+        _ptr(q), _token_stride(q), _ptr(k), _ptr(v), _token_stride(k), _token_stride(v),
+        _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), _ptr(positions), _ptr(cos_sin),
+        int(cos_sin.shape[0]), int(cos_sin.shape[1]), int(style), int(bool(write_k)), n, nb, bs,
+        hq, hkv, d, _dtype_code(q), _stream(stream)))
 
 
 def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
@@ -229,6 +271,7 @@ def _views(layout: BatchLayout, dev: torch.Tensor) -> Dict[str, object]:
         "cu_seqlens_q": arr(layout.off_cu_seqlens_q, layout.num_seqs + 1),
         "cu_seqlens_k": arr(layout.off_cu_seqlens_k, layout.num_seqs + 1),
         "context_lens": arr(layout.off_context_lens, layout.num_seqs),
+        "positions": arr(layout.off_positions, layout.num_slots),
         "block_tables": None,
         "max_seqlen_q": layout.max_seqlen_q, "max_seqlen_k": layout.max_seqlen_k,
         "total_q": layout.total_q, "max_blocks_per_seq": layout.max_blocks_per_seq,

@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <math.h>
+
 #include "pkv.h"
 #include "pkv_internal.h"
 
@@ -80,6 +82,90 @@ extern "C" int pkv_store_kvcache(const void *k, const void *v, int64_t k_token_s
     a.chunks_per_row = (int32_t)(row * es / 16);
     a.num_slots = num_slots;
     return launched(pkv::launch_store(a, (hipStream_t)stream), fn);
+}
+
+extern "C" int pkv_rope_cos_sin_table(float *host_out, int32_t max_positions, int32_t rot_dim,
+                                      double base) {
+    const char *fn = "pkv_rope_cos_sin_table";
+    if (!host_out) return fail(PKV_EINVAL, "%s: null pointer", fn);
+    if (max_positions < 1 || rot_dim < 2 || (rot_dim & 1))
+        return fail(PKV_EINVAL, "%s: need max_positions >= 1 and an even rot_dim >= 2", fn);
+    if (!(base > 0.0) || base == INFINITY) return fail(PKV_EINVAL, "%s: base must be positive", fn);
+    const int half = rot_dim / 2;
+    for (int32_t j = 0; j < half; ++j) {
+        // theta_j(p) = p * base^(-2j / rot_dim), in double
+        const double inv_freq = pow(base, -(2.0 * j) / rot_dim);
+        for (int64_t p = 0; p < max_positions; ++p) {
+            const double ang = (double)p * inv_freq;
+            host_out[p * rot_dim + j] = (float)cos(ang);
+            host_out[p * rot_dim + half + j] = (float)sin(ang);
+        }
+    }
+    return PKV_OK;
+}
+
+extern "C" int pkv_rope_store_kvcache(void *q, int64_t q_token_stride, void *k, const void *v,
+                                      int64_t k_token_stride, int64_t v_token_stride,
+                                      void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                                      const int32_t *positions, const float *cos_sin,
+                                      int32_t max_positions, int32_t rot_dim, int32_t style,
+                                      int32_t write_k, int32_t num_tokens, int32_t num_blocks,
+                                      int32_t block_size, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                      void *stream) {
+    const char *fn = "pkv_rope_store_kvcache";
+    if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
+    if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens < 0", fn);
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PKV_EINVAL, "%s: non-positive shape", fn);
+    if (style != PKV_ROPE_HALF && style != PKV_ROPE_INTERLEAVED)
+        return fail(PKV_EINVAL, "%s: unknown style %d", fn, style);
+    if (max_positions < 1) return fail(PKV_EINVAL, "%s: max_positions < 1", fn);
+    const int es = elem_size(dtype);
+    const int V = 16 / es;   // elements per 16-byte chunk
+    if (rot_dim < 2 || (rot_dim & 1) || rot_dim > head_dim)
+        return fail(PKV_EINVAL, "%s: rot_dim must be even and in [2, head_dim]", fn);
+    if ((head_dim * es) % 16 || rot_dim % (style == PKV_ROPE_HALF ? 2 * V : V))
+        return fail(PKV_EUNSUPPORTED, "%s: head_dim or rot_dim not a whole number of 16-byte chunks", fn);
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    if (num_slots > INT32_MAX) return fail(PKV_EINVAL, "%s: pool has more than 2^31-1 slots", fn);
+    const int64_t qrow = (int64_t)num_q_heads * head_dim, kvrow = (int64_t)num_kv_heads * head_dim;
+    if (q_token_stride < qrow || k_token_stride < kvrow || v_token_stride < kvrow)
+        return fail(PKV_EINVAL, "%s: token stride smaller than a row", fn);
+    if ((q_token_stride * es) % 16 || (k_token_stride * es) % 16 || (v_token_stride * es) % 16)
+        return fail(PKV_EINVAL, "%s: token strides must be multiples of 16 bytes", fn);
+    if (num_tokens == 0) return PKV_OK;
+    if (!q || !k || !v || !k_cache || !v_cache || !slot_mapping || !positions || !cos_sin)
+        return fail(PKV_EINVAL, "%s: null pointer", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(cos_sin))
+        return fail(PKV_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    pkv::RopeStoreArgs a;
+    a.q = (uint8_t *)q;
+    a.k = (uint8_t *)k;
+    a.v = (const uint8_t *)v;
+    a.q_stride_bytes = q_token_stride * es;
+    a.k_stride_bytes = k_token_stride * es;
+    a.v_stride_bytes = v_token_stride * es;
+    a.kc = (uint8_t *)k_cache;
+    a.vc = (uint8_t *)v_cache;
+    a.slots = slot_mapping;
+    a.positions = positions;
+    a.cos_sin = cos_sin;
+    a.max_positions = max_positions;
+    a.rot_dim = rot_dim;
+    a.style = style;
+    a.write_k = write_k != 0;
+    a.d = head_dim;
+    a.row_bytes = kvrow * es;
+    a.num_slots = num_slots;
+    a.r_items = style == PKV_ROPE_HALF ? rot_dim / (2 * V) : rot_dim / V;
+    a.p_items = (head_dim - rot_dim) / V;
+    a.q_items = num_q_heads * a.r_items;
+    a.k_items = num_kv_heads * (a.r_items + a.p_items);
+    a.items_per_token = a.q_items + a.k_items + (int32_t)(kvrow * es / 16);
+    a.total_items = (int64_t)num_tokens * a.items_per_token;
+    return launched(pkv::launch_rope_store(a, dtype, (hipStream_t)stream), fn);
 }
 
 static int check_attention_shape(const char *fn, int32_t dtype, int32_t Hq, int32_t Hkv,

@@ -14,7 +14,8 @@
 // longest one ("prepare_block_tables"), are packed only when the batch reads a
 // cached prefix (total keys > total queries).
 // Decode: one slot per sequence -- the slot of its newest position --, the
-// context length, and the padded block tables.
+// context length, and the padded block tables. Both also pack the position of
+// every slot (the rotary embedding's input).
 #include <limits.h>
 #include <string.h>
 
@@ -49,6 +50,8 @@ void finish_layout(pkv_batch_layout *L, bool prefill) {
     } else {
         L->off_block_tables = -1;
     }
+    L->off_positions = at;
+    at = align256(at + (int64_t)L->num_slots * 4);
     L->total_bytes = at > 0 ? at : 256;
 }
 
@@ -115,6 +118,7 @@ extern "C" int pkv_pack_prefill(int32_t num_seqs, const int32_t *seq_lens,
     int32_t *slots = (int32_t *)(buf + layout->off_slot_mapping);
     int32_t *cu_q = (int32_t *)(buf + layout->off_cu_seqlens_q);
     int32_t *cu_k = (int32_t *)(buf + layout->off_cu_seqlens_k);
+    int32_t *pos = (int32_t *)(buf + layout->off_positions);
     int64_t at = 0;
     cu_q[0] = cu_k[0] = 0;
     for (int32_t s = 0; s < num_seqs; ++s) {
@@ -127,7 +131,10 @@ extern "C" int pkv_pack_prefill(int32_t num_seqs, const int32_t *seq_lens,
             const int64_t base = (int64_t)table[i] * block_size;
             if (table[i] < 0 || base + hi - 1 > INT32_MAX)
                 return pkv_internal_fail(PKV_EINVAL, "pkv_pack_prefill: block id out of range");
-            for (int64_t o = lo; o < hi; ++o) slots[at++] = (int32_t)(base + o);
+            for (int64_t o = lo; o < hi; ++o) {
+                pos[at] = (int32_t)(i * block_size + o);
+                slots[at++] = (int32_t)(base + o);
+            }
         }
         cu_q[s + 1] = cu_q[s] + (int32_t)(n - c);
         cu_k[s + 1] = cu_k[s] + (int32_t)n;
@@ -177,6 +184,7 @@ extern "C" int pkv_pack_decode(int32_t num_seqs, const int32_t *seq_lens, const 
     char *buf = (char *)host_buf;
     int32_t *slots = (int32_t *)(buf + layout->off_slot_mapping);
     int32_t *ctx = (int32_t *)(buf + layout->off_context_lens);
+    int32_t *pos = (int32_t *)(buf + layout->off_positions);
     for (int32_t s = 0; s < num_seqs; ++s) {
         const int64_t n = seq_lens[s];
         const int64_t last_block = (n - 1) / block_size;       // logical block of position n-1
@@ -187,6 +195,7 @@ extern "C" int pkv_pack_decode(int32_t num_seqs, const int32_t *seq_lens, const 
             return pkv_internal_fail(PKV_EINVAL, "pkv_pack_decode: block id out of range");
         slots[s] = (int32_t)slot;
         ctx[s] = (int32_t)n;
+        pos[s] = (int32_t)(n - 1);
     }
     if (layout->has_block_tables) write_tables(layout, bt_ids, bt_offsets, buf);
     return PKV_OK;

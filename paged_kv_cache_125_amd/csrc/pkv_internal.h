@@ -18,6 +18,25 @@ struct StoreArgs {
 };
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream);
 
+struct RopeStoreArgs {
+    uint8_t *q;                  // rotated in place
+    uint8_t *k;                  // read; written back when write_k
+    const uint8_t *v;
+    int64_t q_stride_bytes, k_stride_bytes, v_stride_bytes;
+    uint8_t *kc, *vc;
+    const int32_t *slots, *positions;
+    const float *cos_sin;        // [max_positions][rot_dim]
+    int32_t max_positions, rot_dim, style, write_k, d;
+    int64_t row_bytes;           // one cache slot row (all kv heads)
+    int64_t num_slots;
+    // work items: per token q_items + k_items + v_items
+    int32_t r_items;             // rotated items per head vector
+    int32_t p_items;             // unrotated tail chunks per k head vector
+    int32_t q_items, k_items, items_per_token;
+    int64_t total_items;
+};
+hipError_t launch_rope_store(const RopeStoreArgs &a, int dtype, hipStream_t stream);
+
 struct DecodeArgs {
     const void *q;
     int64_t q_stride;          // elements between consecutive sequences' q rows

@@ -95,6 +95,9 @@ def test_packers_on_presets():
             m = pkv.pack_prefill(w.seq_lens, w.num_cached, w.block_tables, w.block_size, device="cpu")
             ranges = [(s, c, n) for s, (n, c) in enumerate(zip(w.seq_lens, w.num_cached))]
         assert np.array_equal(m["slot_mapping"].numpy(), oracle.slots(ranges, w.block_tables, w.block_size))
+        # positions: the same positions, in the same order as the slots
+        want_pos = np.concatenate([np.arange(b, e) for _, b, e in ranges])
+        assert np.array_equal(m["positions"].numpy(), want_pos)
         if k == 4:
             assert m["block_tables"] is not None and m["total_q"] == 49152
         if k == 3:
@@ -104,7 +107,8 @@ def test_packers_on_presets():
 def test_packed_buffer_is_one_aligned_allocation():
     m = pkv.pack_prefill([300, 5], [256, 0], [[1, 2], [3]], 256, device="cpu")
     L = m["layout"]
-    for off in (L.off_slot_mapping, L.off_cu_seqlens_q, L.off_cu_seqlens_k, L.off_block_tables):
+    for off in (L.off_slot_mapping, L.off_cu_seqlens_q, L.off_cu_seqlens_k, L.off_block_tables,
+                L.off_positions):
         assert off >= 0 and off % 256 == 0
     assert L.total_bytes == m["buffer"].numel()
 
@@ -154,3 +158,14 @@ def test_decode_workspace_and_partition():
     assert P % 16 == 0 and P > 0
     assert pkv.decode_workspace_bytes(4, 100, 4, 2, 64, 16, torch.float32, 256) == 0
     assert pkv.decode_partition_size(4, 100, 4, 2, 64, 16, torch.float32, 48) == 48
+
+
+def test_rope_table_and_argument_checks():
+    t = pkv.rope_cos_sin_table(9, 8, 10000.0, device="cpu")
+    p = np.arange(9)[:, None] * np.power(10000.0, -np.arange(4) * 2.0 / 8)[None, :]
+    np.testing.assert_allclose(t[:, :4].numpy(), np.cos(p), rtol=0, atol=6e-8)
+    np.testing.assert_allclose(t[:, 4:].numpy(), np.sin(p), rtol=0, atol=6e-8)
+    with pytest.raises(pkv.PkvError):
+        pkv.rope_cos_sin_table(4, 7, 10000.0, device="cpu")      # odd rot_dim
+    with pytest.raises(pkv.PkvError):
+        pkv.rope_cos_sin_table(4, 8, -1.0, device="cpu")         # base <= 0

@@ -25,6 +25,13 @@ MUTANTS = {
                             "return (int64_t)table[lb] + p % bs;"),
     "store-half-row": ("(size_t)row_bytes);", "(size_t)row_bytes / 2);"),
     "store-skips-slot-zero": ("if (s < 0)\n            continue;", "if (s <= 0)\n            continue;"),
+    "rope-sign": ("v[ia] = a * c - b * sn;", "v[ia] = a * c + b * sn;"),
+    "rope-exponent": ("pow(base, -2.0 * j / rot_dim)", "pow(base, -1.0 * j / rot_dim)"),
+    "rope-cos-sin-swapped": ("const double c = cos(theta), sn = sin(theta);",
+                             "const double c = sin(theta), sn = cos(theta);"),
+    "rope-position-offset": ("(double)pos[t] * pow", "(double)(pos[t] + 1) * pow"),
+    "rope-half-pairing": ("style == 0 ? j + half : 2 * j + 1", "style == 0 ? half - 1 - j + half : 2 * j + 1"),
+    "rope-interleaved-pairing": ("style == 0 ? j : 2 * j;", "style == 0 ? j : j;"),
 }
 
 

@@ -433,3 +433,75 @@ def test_bf16_rounding_is_round_to_nearest_even():
     want = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
     got = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- rotary embedding
+# The pages feed positions to RoPE without fixing its form; the oracle follows
+# RoFormer (Su et al., 2021). Pinned by closed forms (worked angles, position
+# zero), the rotation's invariants (pair norms, relative-position dot
+# products) and numpy's complex exponential.
+
+def _rand_heads(T, H, d, seed):
+    return np.random.default_rng(seed).standard_normal((T, H, d)).astype(np.float32)
+
+
+@pytest.mark.parametrize("style", [0, 1])
+def test_rope_worked_angles(style):
+    # base 10000, rot_dim 4: pair 0 turns by p rad, pair 1 by p / 100 rad
+    x = np.zeros((2, 1, 6), dtype=np.float32)
+    x[:, 0, 0] = 1.0                      # first element of pair 0
+    x[:, 0, 5] = 3.0                      # past rot_dim: untouched
+    got = oracle.rope(x, [1, 50], 4, 10000.0, style)
+    b0 = 2 if style == 0 else 1           # partner of element 0
+    for t, p in enumerate([1, 50]):
+        want = np.zeros(6)
+        want[0], want[b0], want[5] = math.cos(p), math.sin(p), 3.0
+        np.testing.assert_allclose(got[t, 0], want, rtol=0, atol=1e-15)
+    y = np.zeros((1, 1, 4), dtype=np.float32)
+    y[0, 0, 1] = 1.0                      # first element of pair 1 (style 0) / second of pair 0 (style 1)
+    got = oracle.rope(y, [100], 4, 10000.0, style)[0, 0]
+    if style == 0:
+        np.testing.assert_allclose(got, [0, math.cos(1.0), 0, math.sin(1.0)], rtol=0, atol=1e-15)
+    else:
+        np.testing.assert_allclose(got, [-math.sin(100.0), math.cos(100.0), 0, 0], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("style", [0, 1])
+def test_rope_position_zero_is_identity_and_pairs_keep_their_norm(style):
+    x = _rand_heads(5, 3, 64, 31)
+    np.testing.assert_array_equal(oracle.rope(x, [0] * 5, 64, 1e6, style), x.astype(np.float64))
+    pos = [1, 7, 300, 4095, 32767]
+    got = oracle.rope(x, pos, 48, 1e6, style)
+    xf = x.astype(np.float64)
+    idx = (np.arange(24), np.arange(24) + 24) if style == 0 else (np.arange(0, 48, 2), np.arange(1, 48, 2))
+    n_in = xf[..., idx[0]] ** 2 + xf[..., idx[1]] ** 2
+    n_out = got[..., idx[0]] ** 2 + got[..., idx[1]] ** 2
+    np.testing.assert_allclose(n_out, n_in, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(got[..., 48:], xf[..., 48:])
+
+
+@pytest.mark.parametrize("style", [0, 1])
+def test_rope_dot_products_depend_only_on_relative_position(style):
+    q, k = _rand_heads(1, 2, 32, 32), _rand_heads(1, 2, 32, 33)
+    def dots(pq, pk):
+        a = oracle.rope(q, [pq], 32, 500.0, style)
+        b = oracle.rope(k, [pk], 32, 500.0, style)
+        return (a * b).sum(-1)
+    ref = dots(10, 3)
+    for shift in (1, 17, 1000):
+        np.testing.assert_allclose(dots(10 + shift, 3 + shift), ref, rtol=1e-9, atol=1e-9)
+    assert np.abs(dots(11, 3) - ref).max() > 1e-3   # and they do depend on it
+
+
+@pytest.mark.parametrize("style", [0, 1])
+def test_rope_equals_complex_multiplication(style):
+    x = _rand_heads(4, 2, 16, 34)
+    pos = np.array([0, 3, 1000, 77])
+    got = oracle.rope(x, pos, 16, 10000.0, style)
+    xf = x.astype(np.float64)
+    a, b = (xf[..., :8], xf[..., 8:]) if style == 0 else (xf[..., 0::2], xf[..., 1::2])
+    freq = np.power(10000.0, -np.arange(8) * 2.0 / 16)
+    z = (a + 1j * b) * np.exp(1j * pos[:, None, None] * freq)
+    ga, gb = (got[..., :8], got[..., 8:]) if style == 0 else (got[..., 0::2], got[..., 1::2])
+    np.testing.assert_allclose(ga, z.real, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gb, z.imag, rtol=0, atol=1e-12)
