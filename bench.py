@@ -245,6 +245,42 @@ class Part:
         return d
 
 
+# ----------------------------------------------------------------- host side
+
+def block_manager_host(reps: int = 20) -> dict:
+    """Host cost of the block manager on the prefix-hit step's structure
+    (32 prompts of 2048 tokens, the even ones sharing a 1024-token prefix,
+    block size 256), each repetition on a fresh manager: allocate every prompt
+    (chained hashing of all 65536 tokens; the first sharer registers the
+    prefix, the other 15 find its 4 blocks), gather the tables and pack the
+    step's metadata into a host buffer, then release everything."""
+    import paged_kv_cache_125_amd as pkv
+    rng = np.random.default_rng(1004)
+    prefix = rng.integers(0, 151936, 1024, dtype=np.int64)
+    prompts = [np.concatenate([prefix if s % 2 == 0 else rng.integers(0, 151936, 1024, dtype=np.int64),
+                               rng.integers(0, 151936, 1024, dtype=np.int64)]) for s in range(32)]
+    t_alloc, t_pack, t_free, cached = [], [], [], 0
+    for _ in range(reps):
+        m = pkv.BlockManager(2048, 256)
+        t0 = time.perf_counter()
+        cached = sum(m.allocate(s, p) for s, p in enumerate(prompts))
+        t1 = time.perf_counter()
+        lens, nc, tables = m.gather(range(32))
+        pkv.pack_prefill(lens, nc, tables, 256, device="cpu")
+        t2 = time.perf_counter()
+        for s in range(32):
+            m.deallocate(s)
+        t3 = time.perf_counter()
+        t_alloc.append(t1 - t0)
+        t_pack.append(t2 - t1)
+        t_free.append(t3 - t2)
+    med = lambda v: float(np.median(v)) * 1e6
+    return {"allocate_us": med(t_alloc), "gather_pack_us": med(t_pack), "deallocate_us": med(t_free),
+            "tokens_hashed": 32 * 2048, "cached_tokens_per_step": int(cached),
+            "note": "host only, median of fresh managers; 32 x 2048-token prompts (int64 ids), "
+                    "16 sharing a 1024-token prefix, bs 256; times include the Python binding's calls"}
+
+
 # ----------------------------------------------------------------- oracle side
 
 def cpu_baseline(phase, preset, budget_s):
@@ -586,6 +622,8 @@ def main():
         "secondary": {}, "parts": summaries, "cpu_baselines": cpu,
         "event_timing": {"chunk_steps": EVENT_CHUNK_STEPS, "chunks_with_host_gaps": late},
     }
+    if any(p.preset == 4 for p in parts):
+        line["block_manager_host"] = block_manager_host()
     if pre is not None:
         line["secondary"]["prefill_attention_TFLOPs"] = pre["attention_TFLOPs"]
         line["secondary"]["prefill_frac_of_mfma_peak"] = pre["attention_frac_mfma"]

@@ -240,6 +240,66 @@ int pkv_rope_store_kvcache(void *q, int64_t q_token_stride, void *k, const void 
                            int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Host block manager with a hashed prefix cache ([NV1] BlockManager sections
+ * "1. Block" through "6. 辅助查询方法"; [ES] "PageAttention / 内/显存管理").
+ * Host memory only; no GPU call. Produces each sequence's block table and
+ * cached-token count for pkv_plan_* / pkv_pack_* (pkv_bm_gather writes them
+ * in the packers' CSR form).
+ *
+ * A pool of num_blocks blocks of block_size tokens. Free blocks form a FIFO:
+ * allocation takes the front, release appends to the back. A full block is
+ * identified by a chained hash: xxh64 (seed 0) of the previous block's hash
+ * as 8 little-endian bytes (absent for a sequence's first block) followed by
+ * the block's token ids as little-endian int64 (pkv_block_hash). A hash-table
+ * hit is taken only when the block's recorded hash and tokens both match.
+ *
+ *  pkv_bm_create / pkv_bm_destroy   the manager; handles are not thread-safe.
+ *  pkv_bm_can_allocate(n)           free blocks >= ceil(n / block_size).
+ *  pkv_bm_allocate(seq, tokens, n)  block table for a new sequence (prefill):
+ *      up to the first miss, full blocks found in the cache are shared and
+ *      count as cached tokens (a multiple of block_size, written to
+ *      *num_cached_tokens); every later block is fresh. Full blocks are
+ *      (re)registered. PKV_ENOSPACE if the worst case (no hit) does not fit,
+ *      before anything changes; PKV_EINVAL if seq already holds blocks.
+ *  pkv_bm_append_token(seq, tok)    the sequence grows by one token (after a
+ *      decode step samples it).
+ *  pkv_bm_can_append(seq)           1 if the next pkv_bm_may_append fits.
+ *  pkv_bm_may_append(seq)           before a decode step writes the KV of the
+ *      sequence's newest token: a new block when that token opens one,
+ *      registration of the last block when it fills it. PKV_ENOSPACE when no
+ *      block is free; PKV_EINVAL when the sequence's state is inconsistent.
+ *  pkv_bm_deallocate(seq)           one reference dropped per block, last
+ *      block first; blocks reaching zero go to the back of the FIFO and keep
+ *      their registration until reused. The sequence is forgotten.
+ *  pkv_bm_block_table(seq, out, cap) length of the table (-1 if unknown);
+ *      copied to out when cap is large enough.
+ *  pkv_bm_gather(n, seq_ids, ...)   seq_lens[s], num_cached_tokens[s],
+ *      bt_offsets[0..n] and bt_ids for the packers; PKV_ENOSPACE if
+ *      bt_capacity is too small.
+ * pkv_xxh64 is the hash itself (seed as given), exposed for testing.
+ * -------------------------------------------------------------------------*/
+typedef struct pkv_block_manager pkv_block_manager;
+
+uint64_t pkv_xxh64(const void *data, size_t len, uint64_t seed);
+uint64_t pkv_block_hash(const int64_t *token_ids, int32_t num_tokens, int32_t has_prefix,
+                        uint64_t prefix);
+int pkv_bm_create(int32_t num_blocks, int32_t block_size, pkv_block_manager **out);
+void pkv_bm_destroy(pkv_block_manager *m);
+int32_t pkv_bm_num_free(const pkv_block_manager *m);
+int pkv_bm_can_allocate(const pkv_block_manager *m, int32_t num_tokens);
+int pkv_bm_allocate(pkv_block_manager *m, int64_t seq_id, const int64_t *token_ids,
+                    int32_t num_tokens, int32_t *num_cached_tokens);
+int pkv_bm_append_token(pkv_block_manager *m, int64_t seq_id, int64_t token_id);
+int pkv_bm_can_append(const pkv_block_manager *m, int64_t seq_id);
+int pkv_bm_may_append(pkv_block_manager *m, int64_t seq_id);
+int pkv_bm_deallocate(pkv_block_manager *m, int64_t seq_id);
+int32_t pkv_bm_block_table(const pkv_block_manager *m, int64_t seq_id, int32_t *out,
+                           int32_t capacity);
+int pkv_bm_gather(const pkv_block_manager *m, int32_t num_seqs, const int64_t *seq_ids,
+                  int32_t *seq_lens, int32_t *num_cached_tokens, int64_t *bt_offsets,
+                  int32_t *bt_ids, int64_t bt_capacity);
+
+/* ---------------------------------------------------------------------------
  * Host metadata packing ([NV1] "4. prefill 输入打包" and "5. deocde 输入打包":
  * prepare_block_tables, prepare_prefill, prepare_decode; pinned memory and
  * one asynchronous host-to-device copy.)

@@ -31,6 +31,9 @@ EXPORTED = [
     "pkv_decode_attention_paged", "pkv_decode_partition_size", "pkv_decode_workspace_bytes",
     "pkv_plan_prefill", "pkv_pack_prefill", "pkv_plan_decode", "pkv_pack_decode", "pkv_upload",
     "pkv_rope_cos_sin_table", "pkv_rope_store_kvcache",
+    "pkv_xxh64", "pkv_block_hash", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
+    "pkv_bm_can_allocate", "pkv_bm_allocate", "pkv_bm_append_token", "pkv_bm_can_append",
+    "pkv_bm_may_append", "pkv_bm_deallocate", "pkv_bm_block_table", "pkv_bm_gather",
 ]
 
 
@@ -90,6 +93,33 @@ def lib():
     L.pkv_pack_decode.argtypes = [i32, P, P, P, i32, ctypes.POINTER(BatchLayout), P, sz]
     L.pkv_upload.restype = ctypes.c_int
     L.pkv_upload.argtypes = [P, P, sz, P]
+    u64 = ctypes.c_uint64
+    L.pkv_xxh64.restype = u64
+    L.pkv_xxh64.argtypes = [P, sz, u64]
+    L.pkv_block_hash.restype = u64
+    L.pkv_block_hash.argtypes = [P, i32, i32, u64]
+    L.pkv_bm_create.restype = ctypes.c_int
+    L.pkv_bm_create.argtypes = [i32, i32, ctypes.POINTER(P)]
+    L.pkv_bm_destroy.restype = None
+    L.pkv_bm_destroy.argtypes = [P]
+    L.pkv_bm_num_free.restype = i32
+    L.pkv_bm_num_free.argtypes = [P]
+    L.pkv_bm_can_allocate.restype = ctypes.c_int
+    L.pkv_bm_can_allocate.argtypes = [P, i32]
+    L.pkv_bm_allocate.restype = ctypes.c_int
+    L.pkv_bm_allocate.argtypes = [P, i64, P, i32, ctypes.POINTER(i32)]
+    L.pkv_bm_append_token.restype = ctypes.c_int
+    L.pkv_bm_append_token.argtypes = [P, i64, i64]
+    L.pkv_bm_can_append.restype = ctypes.c_int
+    L.pkv_bm_can_append.argtypes = [P, i64]
+    L.pkv_bm_may_append.restype = ctypes.c_int
+    L.pkv_bm_may_append.argtypes = [P, i64]
+    L.pkv_bm_deallocate.restype = ctypes.c_int
+    L.pkv_bm_deallocate.argtypes = [P, i64]
+    L.pkv_bm_block_table.restype = i32
+    L.pkv_bm_block_table.argtypes = [P, i64, P, i32]
+    L.pkv_bm_gather.restype = ctypes.c_int
+    L.pkv_bm_gather.argtypes = [P, i32, P, P, P, P, P, i64]
     L.pkv_rope_cos_sin_table.restype = ctypes.c_int
     L.pkv_rope_cos_sin_table.argtypes = [P, i32, i32, ctypes.c_double]
     L.pkv_rope_store_kvcache.restype = ctypes.c_int
@@ -141,6 +171,92 @@ def store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cac
                                    _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
                                    int(slot_mapping.numel()), nb, bs, hkv, d, _dtype_code(k_cache),
                                    _stream(stream)))
+
+
+def xxh64(data: bytes, seed: int = 0) -> int:
+    """pkv_xxh64 of a byte string."""
+    buf = ctypes.create_string_buffer(bytes(data), len(data))
+    return int(lib().pkv_xxh64(ctypes.cast(buf, ctypes.c_void_p), len(data), seed))
+
+
+def block_hash(token_ids: Sequence[int], prefix: Optional[int] = None) -> int:
+    """pkv_block_hash: the chained hash of one full block."""
+    import numpy as np
+    t = np.ascontiguousarray(token_ids, dtype=np.int64)
+    return int(lib().pkv_block_hash(ctypes.c_void_p(t.ctypes.data), len(t), prefix is not None,
+                                    0 if prefix is None else int(prefix)))
+
+
+class BlockManager:
+    """The host block manager (pkv_bm_*): block tables and cached-prefix
+    counts for sequences identified by integer ids."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        L = lib()
+        h = ctypes.c_void_p()
+        _check(L.pkv_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)))
+        self._h, self._lib = h, L
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pkv_bm_destroy(h)
+            self._h = None
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pkv_bm_num_free(self._h))
+
+    def can_allocate(self, num_tokens: int) -> bool:
+        return bool(self._lib.pkv_bm_can_allocate(self._h, int(num_tokens)))
+
+    def allocate(self, seq_id: int, token_ids: Sequence[int]) -> int:
+        """Block table for a new sequence; returns its cached-token count."""
+        import numpy as np
+        t = np.ascontiguousarray(token_ids, dtype=np.int64)
+        cached = ctypes.c_int32(0)
+        _check(self._lib.pkv_bm_allocate(self._h, int(seq_id), ctypes.c_void_p(t.ctypes.data),
+                                         len(t), ctypes.byref(cached)))
+        return int(cached.value)
+
+    def append_token(self, seq_id: int, token_id: int) -> None:
+        _check(self._lib.pkv_bm_append_token(self._h, int(seq_id), int(token_id)))
+
+    def can_append(self, seq_id: int) -> bool:
+        return bool(self._lib.pkv_bm_can_append(self._h, int(seq_id)))
+
+    def may_append(self, seq_id: int) -> None:
+        _check(self._lib.pkv_bm_may_append(self._h, int(seq_id)))
+
+    def deallocate(self, seq_id: int) -> None:
+        _check(self._lib.pkv_bm_deallocate(self._h, int(seq_id)))
+
+    def block_table(self, seq_id: int) -> List[int]:
+        import numpy as np
+        n = int(self._lib.pkv_bm_block_table(self._h, int(seq_id), None, 0))
+        if n < 0:
+            raise KeyError(seq_id)
+        out = np.zeros(max(1, n), dtype=np.int32)
+        self._lib.pkv_bm_block_table(self._h, int(seq_id), ctypes.c_void_p(out.ctypes.data), n)
+        return [int(x) for x in out[:n]]
+
+    def gather(self, seq_ids: Sequence[int]):
+        """(seq_lens, num_cached_tokens, block_tables) of the sequences, in order."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = len(ids)
+        lens = np.zeros(max(1, n), dtype=np.int32)
+        cached = np.zeros(max(1, n), dtype=np.int32)
+        off = np.zeros(n + 1, dtype=np.int64)
+        cap = sum(max(0, int(self._lib.pkv_bm_block_table(self._h, int(i), None, 0))) for i in ids)
+        bt = np.zeros(max(1, cap), dtype=np.int32)
+        P = ctypes.c_void_p
+        _check(self._lib.pkv_bm_gather(self._h, n, P(ids.ctypes.data), P(lens.ctypes.data),
+                                       P(cached.ctypes.data), P(off.ctypes.data), P(bt.ctypes.data),
+                                       cap))
+        tables = [[int(x) for x in bt[off[s]:off[s + 1]]] for s in range(n)]
+        return [int(x) for x in lens[:n]], [int(x) for x in cached[:n]], tables
 
 
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1

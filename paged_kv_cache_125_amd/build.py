@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-SOURCES = ["api.hip", "store.hip", "rope.hip", "decode.hip", "prefill.hip", "pack.cpp"]
+SOURCES = ["api.hip", "store.hip", "rope.hip", "decode.hip", "prefill.hip", "pack.cpp", "block_manager.cpp"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

@@ -333,3 +333,37 @@ def test_decode_in_varlen_matches_decode_kernel(cuda):
     d = (out_v.float() - out_d.float()).abs().max().item()
     say(f"  varlen vs decode kernel max |diff| = {d:.3e}")
     assert d <= 2e-2
+
+
+def test_block_manager_prefix_reuse_end_to_end(cuda):
+    say("[gpu] block manager: a second prompt reuses the first one's prefix blocks")
+    from paged_kv_cache_125_amd.step import StepInputs
+    bs, hq, hkv, d = 256, 16, 8, 128
+    scale = 1.0 / np.sqrt(d)
+    m = pkv.BlockManager(16, bs)
+    rng = np.random.default_rng(77)
+    shared = [int(x) for x in rng.integers(0, 150000, 512)]
+    pa = shared + [int(x) for x in rng.integers(0, 150000, 300)]
+    pb = shared + [int(x) for x in rng.integers(0, 150000, 200)]
+    gen = torch.Generator().manual_seed(7)
+    rnd = lambda n, h: torch.randn(n, h, d, generator=gen).to(torch.bfloat16)
+    qa, ka, va = rnd(len(pa), hq), rnd(len(pa), hkv), rnd(len(pa), hkv)
+    kc, vc = alloc_pool(16, bs, hkv, d, torch.bfloat16, "cuda")
+    assert m.allocate(1, pa) == 0
+    lens, nc, tables = m.gather([1])
+    run_step(StepInputs("prefill", lens, nc, tables, bs, scale), qa.cuda(), ka.cuda(), va.cuda(), kc, vc)
+    assert m.allocate(2, pb) == 512
+    assert m.block_table(2)[:2] == m.block_table(1)[:2]
+    qb, kb, vb = rnd(200, hq), rnd(200, hkv), rnd(200, hkv)
+    lens, nc, tables = m.gather([2])
+    out = run_step(StepInputs("prefill", lens, nc, tables, bs, scale), qb.cuda(), kb.cuda(), vb.cuda(),
+                   kc, vc)
+    torch.cuda.synchronize()
+    # the oracle recomputes prompt B in full: its first 512 keys are A's
+    q_full = torch.zeros(len(pb), hq, d, dtype=torch.bfloat16)
+    q_full[512:] = qb
+    want = oracle.attention(q_full, [len(pb)], [len(pb)], hkv, scale,
+                            k=torch.cat([ka[:512], kb]), v=torch.cat([va[:512], vb]))[512:]
+    err = max_abs_err(out, want)
+    say(f"  max |err| = {err:.3e}")
+    assert err <= 2e-2
