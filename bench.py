@@ -55,6 +55,8 @@ WORKLOADS = {
     "mixed": [("prefill", 7)],
     # preset 3's step with the rotary embedding fused into the store
     "rope-store": [("prefill+rope", 3)],
+    # preset 2's decode, plus 28-layer decode steps eager vs replayed hipGraphs
+    "decode-graph": [("decode", 2)],
 }
 
 
@@ -279,6 +281,62 @@ def block_manager_host(reps: int = 20) -> dict:
             "tokens_hashed": 32 * 2048, "cached_tokens_per_step": int(cached),
             "note": "host only, median of fresh managers; 32 x 2048-token prompts (int64 ids), "
                     "16 sharing a 1024-token prefix, bs 256; times include the Python binding's calls"}
+
+
+def decode_graph_compare(num_layers: int = 28, batches=(1, 8, 64), steps: int = 30) -> dict:
+    """Decode steps of `num_layers` layers (store + attention per layer, each
+    layer with its own pool) run eagerly -- one C-ABI call per kernel -- and as
+    a replayed hipGraph of the batch's bucket, on preset 2's first B
+    sequences. Both include the step's metadata packing and upload; the
+    layers' q, k, v stay resident (in a model, earlier kernels of the step
+    produce them). Wall time per step, synchronized at both ends."""
+    import paged_kv_cache_125_amd as pkv
+    from paged_kv_cache_125_amd.graphs import DecodeGraphs, bucket_for
+    from paged_kv_cache_125_amd.step import alloc_pool, write_ranges
+    from workloads import make_workload, restrict
+    full = make_workload(2, device="cuda")
+    res = {}
+    for B in batches:
+        w = restrict(full, list(range(B)), device="cuda")
+        layers = []
+        for _ in range(num_layers):
+            kc, vc = alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype, "cuda")
+            write_ranges(w.hist, w.block_tables, w.block_size, w.k_hist, w.v_hist, kc, vc)
+            layers.append((kc, vc))
+        maxb = max(len(t) for t in w.block_tables)
+        g = DecodeGraphs(layers, w.num_q_heads, max_context_len=4096, max_blocks_per_seq=maxb,
+                         scale=w.scale, buckets=[bucket_for(B)])
+        qs, ks, vs = [w.q] * num_layers, [w.k_new] * num_layers, [w.v_new] * num_layers
+        meta = pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cuda")
+        g.prepare(qs, ks, vs, meta["slot_mapping"], meta["context_lens"], meta["block_tables"])
+
+        def eager():
+            m = pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cuda")
+            g.run_eager(qs, ks, vs, m["slot_mapping"], m["context_lens"], m["block_tables"],
+                        m["max_seqlen_k"])
+
+        def graph():
+            m = pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cuda")
+            g.replay(g.prepare_meta(m["slot_mapping"], m["context_lens"], m["block_tables"]))
+
+        times = {}
+        for name, fn in (("eager", eager), ("graph", graph), ("eager", eager), ("graph", graph)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+            times[name] = (time.perf_counter() - t0) / steps * 1e3   # the second round counts
+        res[f"B{B}"] = {"eager_ms_per_step": times["eager"], "graph_ms_per_step": times["graph"],
+                        "speedup": times["eager"] / times["graph"], "bucket": bucket_for(B),
+                        "context_tokens": int(sum(w.seq_lens))}
+        del layers, g
+        torch.cuda.empty_cache()
+    return {"layers": num_layers, "per_batch": res,
+            "note": "decode attention side of one step (store + attention per layer) for the first B "
+                    "sequences of preset 2; wall clock per step incl. metadata pack+upload"}
 
 
 # ----------------------------------------------------------------- oracle side
@@ -624,6 +682,9 @@ def main():
     }
     if any(p.preset == 4 for p in parts):
         line["block_manager_host"] = block_manager_host()
+    if args.workload == "decode-graph":
+        log("[bench] 28-layer decode steps: eager vs hipGraph")
+        line["decode_graph"] = decode_graph_compare()
     if pre is not None:
         line["secondary"]["prefill_attention_TFLOPs"] = pre["attention_TFLOPs"]
         line["secondary"]["prefill_frac_of_mfma_peak"] = pre["attention_frac_mfma"]
