@@ -52,7 +52,7 @@ WORKLOADS = {
     # decode rows through the varlen prefill call, beside the decode kernel on
     # the same batch; and a mixed step (decode rows + two prompt chunks)
     "decode-in-varlen": [("decode", 2), ("prefill", 6)],
-    "mixed": [("prefill", 7)],
+    "mixed": [("prefill", 7), ("prefill+split", 7)],
     # preset 3's step with the rotary embedding fused into the store
     "rope-store": [("prefill+rope", 3)],
     # preset 2's decode, plus 28-layer decode steps eager vs replayed hipGraphs
@@ -131,8 +131,11 @@ class Part:
         from paged_kv_cache_125_amd.step import alloc_pool, step_inputs_of, write_ranges
         from workloads import make_workload
         self.pkv = pkv
-        # "prefill+rope": the store is the fused rotary embedding + store
+        # "prefill+rope": the store is the fused rotary embedding + store;
+        # "prefill+split": a mixed step's decode rows (first) go through the
+        # decode kernel, the rest through the varlen call
         self.rope = phase.endswith("+rope")
+        self.split = phase.endswith("+split")
         phase = phase.split("+")[0]
         self.phase, self.preset = phase, preset
         self.copies = []
@@ -146,6 +149,16 @@ class Part:
             self.copies.append((w, kc, vc, out))
         self.w = w
         self.s = step_inputs_of(w)
+        if self.split:
+            from paged_kv_cache_125_amd.step import StepInputs, decode_rows_first
+            nd = self.nd = decode_rows_first(self.s)
+            self.sd = StepInputs("decode", self.s.seq_lens[:nd], self.s.num_cached[:nd],
+                                 self.s.block_tables[:nd], w.block_size, w.scale)
+            self.sp = StepInputs("prefill", self.s.seq_lens[nd:], self.s.num_cached[nd:],
+                                 self.s.block_tables[nd:], w.block_size, w.scale)
+            need = pkv.decode_workspace_bytes(nd, max(self.sd.seq_lens), w.num_q_heads,
+                                              w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+            self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
         if phase == "decode":
             need = pkv.decode_workspace_bytes(len(w.seq_lens), max(w.seq_lens), w.num_q_heads,
                                               w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
@@ -166,6 +179,16 @@ class Part:
         """n (pinned host, device) metadata buffers, one per pass, so that the
         passes allocate nothing (a new pinned allocation can stall the host)."""
         pkv, s = self.pkv, self.s
+        if self.split:
+            md = pkv.pack_decode(self.sd.seq_lens, self.sd.block_tables, s.block_size, device="cpu")
+            mp = pkv.pack_prefill(self.sp.seq_lens, self.sp.num_cached, self.sp.block_tables,
+                                  s.block_size, device="cpu")
+            nd, npf = int(md["layout"].total_bytes), int(mp["layout"].total_bytes)
+            self.ring = [((torch.empty(nd, dtype=torch.uint8, pin_memory=True),
+                           torch.empty(nd, dtype=torch.uint8, device="cuda")),
+                          (torch.empty(npf, dtype=torch.uint8, pin_memory=True),
+                           torch.empty(npf, dtype=torch.uint8, device="cuda"))) for _ in range(n)]
+            return
         if self.phase == "decode":
             meta = pkv.pack_decode(s.seq_lens, s.block_tables, s.block_size, device="cpu")
         else:
@@ -179,8 +202,28 @@ class Part:
         4 torch.cuda.Event or None."""
         pkv, s = self.pkv, self.s
         w, kc, vc, out = self.copies[i % len(self.copies)]
-        hb, db = self.ring[i]
         rec = (lambda j: events[j].record()) if events else (lambda j: None)
+        if self.split:
+            (hd, dd), (hp, dp) = self.ring[i]
+            nd = self.nd
+            rec(0)
+            md = pkv.pack_decode(self.sd.seq_lens, self.sd.block_tables, s.block_size,
+                                 host_buffer=hd, dev_buffer=dd)
+            mp = pkv.pack_prefill(self.sp.seq_lens, self.sp.num_cached, self.sp.block_tables,
+                                  s.block_size, host_buffer=hp, dev_buffer=dp)
+            rec(1)
+            pkv.store_kvcache(w.k_new[:nd], w.v_new[:nd], kc, vc, md["slot_mapping"])
+            pkv.store_kvcache(w.k_new[nd:], w.v_new[nd:], kc, vc, mp["slot_mapping"])
+            rec(2)
+            pkv.decode_attention_paged(w.q[:nd], kc, vc, md["block_tables"], md["context_lens"],
+                                       md["max_seqlen_k"], s.scale, out=out[:nd], workspace=self.ws)
+            pkv.prefill_attention_varlen(w.q[nd:], mp["cu_seqlens_q"], mp["cu_seqlens_k"],
+                                         mp["max_seqlen_q"], mp["max_seqlen_k"], s.scale,
+                                         k_cache=kc, v_cache=vc, block_tables=mp["block_tables"],
+                                         out=out[nd:])
+            rec(3)
+            return (md, mp)
+        hb, db = self.ring[i]
         rec(0)
         if self.phase == "decode":
             meta = pkv.pack_decode(s.seq_lens, s.block_tables, s.block_size, host_buffer=hb, dev_buffer=db)
@@ -224,7 +267,8 @@ class Part:
         t_store = float(np.mean(self.times["store"]))
         t_pack = float(np.mean(self.times["pack"]))
         sb = rope_store_bytes(w) if self.rope else store_bytes(w)
-        d = {"workload": w.name + ("+rope" if self.rope else ""), "preset": self.preset,
+        d = {"workload": w.name + ("+rope" if self.rope else "") + ("+split" if self.split else ""),
+             "preset": self.preset,
              "phase": self.phase, "store": "rope_store_kvcache" if self.rope else "store_kvcache",
              "num_seqs": len(w.seq_lens), "tokens_q": w.total_q,
              "context_tokens": int(sum(w.seq_lens)),
@@ -633,7 +677,8 @@ def main():
     if not args.no_cpu_baseline:
         for p in parts:
             log(f"[bench] oracle cpu baseline: {p.phase} preset {p.preset}")
-            cpu[p.phase] = cpu_baseline(p.phase, p.preset, args.cpu_budget)
+            if p.phase not in cpu:
+                cpu[p.phase] = cpu_baseline(p.phase, p.preset, args.cpu_budget)
 
     dec = next((s for s in summaries if s["phase"] == "decode"), None)
     pre = next((s for s in summaries if s["phase"] == "prefill"), None)

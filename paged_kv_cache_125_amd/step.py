@@ -84,6 +84,42 @@ def run_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
                                     k=k_new, v=v_new, out=out, stream=stream)
 
 
+def decode_rows_first(s: StepInputs) -> int:
+    """Number of leading sequences of a prefill step that are decode rows
+    (exactly one new token on top of a cached context)."""
+    n = 0
+    for L, c in zip(s.seq_lens, s.num_cached):
+        if L - c != 1 or c < 1:
+            break
+        n += 1
+    return n
+
+
+def run_mixed_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """A mixed (chunked-prefill) step whose decode rows come first: those go
+    through the decode kernel -- the K/V of a kv head streamed once for its
+    whole query-head group and split over every SIMD -- and the prompts and
+    prompt chunks that follow through the varlen call. Same results as
+    ``run_step`` on the whole batch."""
+    nd = decode_rows_first(s)
+    if nd == 0 or nd == len(s.seq_lens):
+        return run_step(s if nd == 0 else StepInputs("decode", s.seq_lens, s.num_cached,
+                                                        s.block_tables, s.block_size, s.scale),
+                        q, k_new, v_new, k_cache, v_cache, out=out, workspace=workspace, stream=stream)
+    if out is None:
+        out = torch.empty_like(q)
+    dec = StepInputs("decode", s.seq_lens[:nd], s.num_cached[:nd], s.block_tables[:nd],
+                     s.block_size, s.scale)
+    pre = StepInputs("prefill", s.seq_lens[nd:], s.num_cached[nd:], s.block_tables[nd:],
+                     s.block_size, s.scale, s.use_block_tables)
+    run_step(dec, q[:nd], k_new[:nd], v_new[:nd], k_cache, v_cache, out=out[:nd],
+             workspace=workspace, stream=stream)
+    run_step(pre, q[nd:], k_new[nd:], v_new[nd:], k_cache, v_cache, out=out[nd:], stream=stream)
+    return out
+
+
 def step_inputs_of(w, partition_size: int = 0) -> StepInputs:
     """StepInputs from any object with the batch fields (e.g. a seeded workload)."""
     return StepInputs(phase=w.phase, seq_lens=list(w.seq_lens), num_cached=list(w.num_cached),
