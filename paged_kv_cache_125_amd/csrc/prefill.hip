@@ -356,6 +356,36 @@ void prefill_mfma_kernel(PrefillArgs a) {
         __syncthreads();
     }
 
+    if constexpr (RB == 1) {
+        // Through LDS (the tile buffers are free after the last barrier): the
+        // wave's 32 x 128 output tile goes in with 8-byte writes, rows 272
+        // bytes apart, and comes back as whole 256-byte rows, so each global
+        // store writes four full rows instead of 32 scattered 16-byte pieces.
+        constexpr int kPitch = 272;
+        uint8_t *stg = &lds[0][0] + kPitch * 32 * wave;
+        const float lt = xor32_sum(l[0]);
+        const float inv = row_ok[0] ? 1.f / lt : 0.f;
+        // o[0][nt][4*g + c] = O[row][d = 32*nt + 8*g + 4*j + c]
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = pack_bf16x2(o[0][nt][4 * g] * inv, o[0][nt][4 * g + 1] * inv);
+                w[1] = pack_bf16x2(o[0][nt][4 * g + 2] * inv, o[0][nt][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2 *>(stg + r32 * kPitch + 2 * (32 * nt + 8 * g + 4 * j)) = w;
+            }
+        const int rbase = q0 + 32 * wave;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int rr = 4 * i + (lane >> 4), chunk = lane & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rr * kPitch + 16 * chunk);
+            if (rbase + rr < Lq) {
+                uint16_t *out = (uint16_t *)a.out + ((int64_t)(q_start + rbase + rr) * a.Hq + h) * kPfD;
+                *reinterpret_cast<u32x4 *>(out + 8 * chunk) = v;
+            }
+        }
+    } else {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float lt = xor32_sum(l[rb]);
@@ -373,6 +403,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 w[1] = pack_bf16x2(o[rb][nt][4 * g + 2] * inv, o[rb][nt][4 * g + 3] * inv);
                 *reinterpret_cast<u32x2 *>(out + 32 * nt + 8 * g + 4 * j) = w;
             }
+    }
     }
 }
 
