@@ -77,7 +77,8 @@ const char *pkv_last_error(void);
  * For i in [0, num_tokens): s = slot_mapping[i]; if 0 <= s < num_blocks *
  * block_size, copy k row i ([num_kv_heads, head_dim] elements) bit for bit to
  * k_cache viewed as [num_blocks * block_size, num_kv_heads, head_dim] row s,
- * and likewise v -> v_cache. Negative slots (padding) are skipped.
+ * and likewise v -> v_cache. Negative slots (padding) are skipped: nothing is
+ * written for them (their k/v rows must still be readable memory).
  *
  *  k, v            [num_tokens, num_kv_heads, head_dim] with token strides
  *                  k_token_stride / v_token_stride (elements; the rows of one

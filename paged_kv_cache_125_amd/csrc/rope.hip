@@ -141,10 +141,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(RopeStoreArgs 
         return;
     }
     u -= a.k_items;
-    if (!store) return;
-    // v: chunk u of the row (all heads), copied bit for bit
-    const uint8_t *src = a.v + (int64_t)t * a.v_stride_bytes + (int64_t)u * 16;
-    st16(a.vc + (int64_t)slot * a.row_bytes + (int64_t)u * 16, ld16(src));
+    // v: chunk u of the row (all heads), copied bit for bit; the load is
+    // issued with the slot's, only the store depends on it
+    const u32x4 vv = ld16(a.v + (int64_t)t * a.v_stride_bytes + (int64_t)u * 16);
+    if (store) st16(a.vc + (int64_t)slot * a.row_bytes + (int64_t)u * 16, vv);
 }
 
 hipError_t launch_rope_store(const RopeStoreArgs &a, int dtype, hipStream_t stream) {

@@ -10,7 +10,9 @@
 // and of the V row is one work item. Consecutive lanes take consecutive chunks
 // of one row, so each wave instruction moves whole 64-byte segments; every
 // thread keeps kStoreUnroll items (2 * kStoreUnroll loads) in flight before
-// its stores.
+// its stores. The K/V loads do not wait for the slot: they are issued with
+// the slot load (every token row is readable), and only the stores depend on
+// it.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -26,6 +28,7 @@ __global__ __launch_bounds__(kStoreThreads) void store_kvcache_kernel(StoreArgs 
     const int64_t total = (int64_t)a.num_tokens * a.chunks_per_row;
     const int64_t base = (int64_t)blockIdx.x * (kStoreThreads * kStoreUnroll) + threadIdx.x;
     const int64_t row_bytes = (int64_t)a.chunks_per_row * 16;
+    const bool narrow = total <= 0x7fffffffLL;   // item indices fit 32-bit division
     u32x4 kx[kStoreUnroll], vx[kStoreUnroll];
     int64_t dst[kStoreUnroll];
 #pragma unroll
@@ -33,14 +36,18 @@ __global__ __launch_bounds__(kStoreThreads) void store_kvcache_kernel(StoreArgs 
         const int64_t item = base + (int64_t)u * kStoreThreads;
         dst[u] = -1;
         if (item < total) {
-            const int32_t t = (int32_t)(item / a.chunks_per_row);
-            const int32_t c = (int32_t)(item - (int64_t)t * a.chunks_per_row);
-            const int32_t s = a.slots[t];
-            if (s >= 0 && s < a.num_slots) {
-                kx[u] = ld16(a.k + t * a.k_stride_bytes + c * 16);
-                vx[u] = ld16(a.v + t * a.v_stride_bytes + c * 16);
-                dst[u] = (int64_t)s * row_bytes + c * 16;
+            int32_t t, c;
+            if (narrow) {
+                t = (int32_t)item / a.chunks_per_row;
+                c = (int32_t)item - t * a.chunks_per_row;
+            } else {
+                t = (int32_t)(item / a.chunks_per_row);
+                c = (int32_t)(item - (int64_t)t * a.chunks_per_row);
             }
+            const int32_t s = a.slots[t];
+            kx[u] = ld16(a.k + t * a.k_stride_bytes + c * 16);
+            vx[u] = ld16(a.v + t * a.v_stride_bytes + c * 16);
+            if (s >= 0 && s < a.num_slots) dst[u] = (int64_t)s * row_bytes + c * 16;
         }
     }
 #pragma unroll
