@@ -131,6 +131,10 @@ PREFILL_EDGES = [
     ([17, 18], [16, 16], 4, 2, 128, 16, torch.bfloat16, True),                    # Lq 1 and 2
     ([150, 70], [64, 0], 8, 4, 128, 2, torch.bfloat16, True),                     # blocks of 2 keys
     ([600, 129, 64], [320, 64, 0], 8, 2, 128, 64, torch.bfloat16, True),          # blocks of 64 keys
+    ([1100, 300], [0, 100], 32, 2, 128, 1024, torch.bfloat16, True),              # blocks of 1024, group 16
+    ([513, 200], [0, 0], 32, 4, 128, 128, torch.bfloat16, True),                  # blocks of 128, group 8
+    ([90, 250], [40, 0], 8, 2, 128, 32, torch.bfloat16, True),                    # blocks of 32 keys
+    ([4096], [2048], 4, 1, 128, 256, torch.bfloat16, True),                       # 2048 rows over 4096 keys
 ]
 
 
