@@ -128,8 +128,11 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int kend = min(Lk, off + min(q0 + BM, Lq));   // keys this block needs
     const int n_kt = (kend + kPfBN - 1) / kPfBN;
     // Position of the wave's last row: tiles starting past it hold only masked
-    // keys for this wave, which skips their arithmetic (not their loads).
+    // keys for this wave, which skips their arithmetic (not their loads). A
+    // wave whose rows all lie past the sequence's end (the last query block of
+    // a sequence, or a short one such as a decode row) skips all of it.
     const int pos_last = off + q0 + 32 * RB * (wave + 1) - 1;
+    const bool wave_rows = q0 + 32 * RB * wave < Lq;
 
     // Tile loads go global -> LDS directly (buffer_load_dwordx4 ... lds), no
     // registers in between. Instruction i of wave w fills LDS bytes
@@ -233,7 +236,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
         if (more) load_tile(k0 + kPfBN, nxt);
         const uint8_t *Ks = cur;
         const uint8_t *Vs = cur + kTileBytes;
-        if (!decltype(masked)::value || k0 <= pos_last) {
+        if (wave_rows && (!decltype(masked)::value || k0 <= pos_last)) {
             // S^T tiles: st[rb][mt][r] = S[row r32 of block rb][key k0 + 32*mt + 8*(r/4) + 4*j + r%4].
             // Every K operand read from LDS feeds both row blocks.
             f32x16 st[RB][2];
