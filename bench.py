@@ -25,6 +25,7 @@ cached 1024-token prefix on half of them).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -123,6 +124,13 @@ def prefill_flops(w) -> float:
 
 # ----------------------------------------------------------------- GPU side
 
+def _pinned(nbytes: int) -> torch.Tensor:
+    """A pinned staging buffer, written once here: the first write to each
+    page of a new pinned allocation faults it in (about 1 us a page), a cost
+    a serving loop that reuses its staging buffers pays only once."""
+    return torch.empty(nbytes, dtype=torch.uint8, pin_memory=True).zero_()
+
+
 class Part:
     """One workload of the step, with `ncopies` resident copies of its inputs."""
 
@@ -184,18 +192,17 @@ class Part:
             mp = pkv.pack_prefill(self.sp.seq_lens, self.sp.num_cached, self.sp.block_tables,
                                   s.block_size, device="cpu")
             nd, npf = int(md["layout"].total_bytes), int(mp["layout"].total_bytes)
-            self.ring = [((torch.empty(nd, dtype=torch.uint8, pin_memory=True),
-                           torch.empty(nd, dtype=torch.uint8, device="cuda")),
-                          (torch.empty(npf, dtype=torch.uint8, pin_memory=True),
-                           torch.empty(npf, dtype=torch.uint8, device="cuda"))) for _ in range(n)]
+            self.ring = [((_pinned(nd), torch.empty(nd, dtype=torch.uint8, device="cuda")),
+                          (_pinned(npf), torch.empty(npf, dtype=torch.uint8, device="cuda")))
+                         for _ in range(n)]
             return
         if self.phase == "decode":
             meta = pkv.pack_decode(s.seq_lens, s.block_tables, s.block_size, device="cpu")
         else:
             meta = pkv.pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size, device="cpu")
         nbytes = int(meta["layout"].total_bytes)
-        self.ring = [(torch.empty(nbytes, dtype=torch.uint8, pin_memory=True),
-                      torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(n)]
+        self.ring = [(_pinned(nbytes), torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
+                     for _ in range(n)]
 
     def run(self, i, events):
         """Pass i (each pass has its own metadata buffers); events is a list of
@@ -620,7 +627,12 @@ def main():
     del metas
 
     # Whole steps, wall clock: host packing, uploads and every kernel, with a
-    # synchronize on both sides.
+    # synchronize on both sides. The objects made during set-up (torch's own
+    # included, ~170k) are collected and frozen first, so that the garbage
+    # collector does not traverse them all inside the timed pass (a full
+    # collection there stalls the host for ~37 ms, longer than the 50 steps).
+    gc.collect()
+    gc.freeze()
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()

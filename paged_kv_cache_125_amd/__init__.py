@@ -369,13 +369,18 @@ def decode_attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
 
 
 def _csr(block_tables: Sequence[Sequence[int]]):
+    """The per-sequence tables as one int32 id array plus int64 offsets, built
+    in two passes over the Python lists (no per-row temporary arrays)."""
+    import itertools
     import numpy as np
-    lens = np.fromiter((len(t) for t in block_tables), dtype=np.int64, count=len(block_tables))
-    off = np.zeros(len(block_tables) + 1, dtype=np.int64)
-    np.cumsum(lens, out=off[1:])
-    ids = np.zeros(max(1, int(off[-1])), dtype=np.int32)
-    if off[-1] > 0:
-        ids[:off[-1]] = np.concatenate([np.asarray(t, dtype=np.int32) for t in block_tables])
+    n = len(block_tables)
+    off = np.empty(n + 1, dtype=np.int64)
+    off[0] = 0
+    np.cumsum(np.fromiter(map(len, block_tables), dtype=np.int64, count=n), out=off[1:])
+    total = int(off[-1])
+    if total == 0:
+        return np.zeros(1, dtype=np.int32), off
+    ids = np.fromiter(itertools.chain.from_iterable(block_tables), dtype=np.int32, count=total)
     return ids, off
 
 
