@@ -467,6 +467,26 @@ COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
 CALIBRATION_BYTES = 1 << 30     # the plain device copy timed under the counters
 
 
+def device_copy_rate(reps: int = 5) -> float:
+    """GB/s (bytes read + bytes written) of a 1 GiB device-to-device copy,
+    the runtime's own copy kernel, timed with events: a measured ceiling for
+    streaming kernels on this GPU, reported beside the published HBM peak."""
+    src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * CALIBRATION_BYTES / sec / 1e9
+
+
 def _source_sha(kernel_file: str) -> str:
     src = os.path.join(ROOT, "paged_kv_cache_125_amd", "csrc", kernel_file)
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -606,6 +626,8 @@ def main():
         log(f"[bench] setting up {phase} preset {preset} ({nc} copies)")
         parts.append(Part(phase, preset, nc))
 
+    copy_gbps = device_copy_rate()
+    log(f"[bench] 1 GiB device copy: {copy_gbps:.0f} GB/s (read + write)")
     if args.copy_calibration:
         src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -747,6 +769,8 @@ def main():
         line["secondary"]["prefill_frac_of_mfma_peak"] = pre["attention_frac_mfma"]
     if dec is not None:
         line["secondary"]["decode_frac_of_hbm_peak"] = dec["attention_frac_hbm"]
+    # what a plain streaming kernel reaches on this GPU, beside the published peak
+    line["secondary"]["device_copy_GBps"] = copy_gbps
     print(json.dumps(line), flush=True)
 
 
