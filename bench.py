@@ -53,7 +53,7 @@ WORKLOADS = {
     # decode rows through the varlen prefill call, beside the decode kernel on
     # the same batch; and a mixed step (decode rows + two prompt chunks)
     "decode-in-varlen": [("decode", 2), ("prefill", 6)],
-    "mixed": [("prefill", 7)],
+    "mixed": [("prefill", 7), ("prefill+split", 7)],
     # preset 3's step with the rotary embedding fused into the store
     "rope-store": [("prefill+rope", 3)],
     # preset 2's decode, plus 28-layer decode steps eager vs replayed hipGraphs

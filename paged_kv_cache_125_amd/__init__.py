@@ -15,7 +15,8 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Dict, List, Optional, Sequence
+import threading
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
@@ -405,6 +406,25 @@ def _views(layout: BatchLayout, dev: torch.Tensor) -> Dict[str, object]:
     return out
 
 
+# Pinned staging buffers that the binding allocated itself, each held until an
+# event recorded right after its upload has completed. torch's pinned-memory
+# cache knows nothing of a hipMemcpyAsync issued through the C ABI: a buffer
+# freed while such a copy is still queued goes straight back to its free list,
+# the next pinned allocation of the same size class receives it, and the
+# packer then overwrites the bytes the queued copy has yet to read (the device
+# metadata of the earlier step would hold the later step's values).
+_staging: List[Tuple[torch.Tensor, object]] = []
+_staging_lock = threading.Lock()
+
+
+def _hold_until_uploaded(host: torch.Tensor, stream) -> None:
+    ev = torch.cuda.Event()
+    ev.record(torch.cuda.current_stream() if stream is None else stream)
+    with _staging_lock:
+        _staging[:] = [(h, e) for h, e in _staging if not e.query()]
+        _staging.append((host, ev))
+
+
 def _pack(prefill: bool, seq_lens, num_cached, block_tables, block_size: int, device,
           stream=None, host_buffer: Optional[torch.Tensor] = None,
           dev_buffer: Optional[torch.Tensor] = None) -> Dict[str, object]:
@@ -448,8 +468,10 @@ def _pack(prefill: bool, seq_lens, num_cached, block_tables, block_size: int, de
                 raise ValueError(f"dev_buffer must be a contiguous device uint8 tensor of >= {nbytes} bytes")
             dev = dev_buffer[:nbytes]
         _check(L.pkv_upload(P(host.data_ptr()), P(dev.data_ptr()), nbytes, _stream(stream)))
+        if host_buffer is None:
+            _hold_until_uploaded(host, stream)
     res = _views(layout, dev)
-    res["host_buffer"] = host   # keep the pinned source alive until the copy has run
+    res["host_buffer"] = host
     res["layout"] = layout
     return res
 
@@ -464,8 +486,9 @@ def pack_prefill(seq_lens: Sequence[int], num_cached: Sequence[int],
 
     ``host_buffer`` (pinned CPU uint8) and ``dev_buffer`` (device uint8), when
     given, are used as the staging and destination buffers instead of new
-    allocations; the caller must not reuse ``host_buffer`` before the stream
-    has run the copy."""
+    allocations; the caller must not reuse or free ``host_buffer`` before the
+    stream has run the copy. A staging buffer the binding allocates itself is
+    held by the binding until the copy has run."""
     return _pack(True, seq_lens, num_cached, block_tables, block_size, device, stream,
                  host_buffer, dev_buffer)
 

@@ -102,9 +102,13 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int q_start = a.cu_q[s];
     const int Lq = a.cu_q[s + 1] - q_start;
     const int q0 = qt * BM;
-    if (q0 >= Lq) return;
+    // Rows outside [0, total_q) of q and out are never touched, whatever
+    // cu_seqlens_q holds.
+    if (q0 >= Lq || q_start < 0 || q_start > a.total_q - Lq) return;
     const int k_start = a.cu_k[s];
     const int Lk = a.cu_k[s + 1] - k_start;
+    // Contiguous keys are this call's rows (Lk == Lq), so they too lie in [0, total_q).
+    if (SRC == kContiguous && (k_start < 0 || k_start > a.total_q - Lk)) return;
     const int off = Lk - Lq;
     const int r32 = lane & 31, j = lane >> 5;
     // The wave owns rows q0 + 32*RB*wave + 32*rb + r32, rb < RB.
@@ -435,9 +439,10 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a) {
     const int row = blockIdx.x * 4 + wave, h = blockIdx.y, s = blockIdx.z;
     const int q_start = a.cu_q[s];
     const int Lq = a.cu_q[s + 1] - q_start;
-    if (row >= Lq) return;
+    if (row >= Lq || q_start < 0 || q_start > a.total_q - Lq) return;
     const int k_start = a.cu_k[s];
     const int Lk = a.cu_k[s + 1] - k_start;
+    if (!a.paged && (k_start < 0 || k_start > a.total_q - Lk)) return;
     const int pos = Lk - Lq + row;
     const int kvh = h / a.group;
     const T *q = (const T *)a.q + (int64_t)(q_start + row) * a.q_stride + (int64_t)h * D;

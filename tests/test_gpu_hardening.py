@@ -1,0 +1,90 @@
+"""Regression tests for two ways bad step metadata could reach the kernels.
+
+1. Staging lifetime. The binding packs a step's metadata into a pinned host
+   buffer and uploads it with pkv_upload (hipMemcpyAsync). When the binding
+   allocated that buffer itself and the caller keeps only the device views,
+   the buffer used to be freed at once; torch's pinned-memory cache then gave
+   it to the next pack of the same size class, which overwrote it before the
+   queued copy had run, so the earlier step's device metadata held the later
+   step's values. The binding now holds such buffers until the copy has run.
+2. Prefill bounds. The prefill kernels index q, out and contiguous k/v rows
+   with cu_seqlens read on the device. A sequence whose rows do not fit in
+   [0, total_q) is now skipped instead of read and written out of range.
+
+Only packs, uploads, a spin kernel and prefill calls whose out-of-range rows
+stay inside the same small tensors run here."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_125_amd as pkv
+from gpu_helpers import max_abs_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv.lib()
+    return torch.device("cuda")
+
+
+def test_staging_buffer_outlives_its_queued_upload(cuda):
+    say("[gpu] pinned staging buffer held until its upload has run")
+    bs = 16
+    lens = [100 + i for i in range(32)]
+    tables_a = [list(range(i * 80, i * 80 + -(-n // bs))) for i, n in enumerate(lens)]
+    tables_b = [list(range(5000 + i * 80, 5000 + i * 80 + -(-n // bs))) for i, n in enumerate(lens)]
+    for trial in range(3):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)       # the uploads queue behind a few ms of spinning
+        m = pkv.pack_decode(lens, tables_a, bs, device="cuda")
+        bt_a = m["block_tables"]             # keep only the device view, as a step does
+        del m
+        m2 = pkv.pack_decode(lens, tables_b, bs, device="cuda")   # same layout size
+        torch.cuda.synchronize()
+        got = bt_a.cpu()
+        for i, t in enumerate(tables_a):
+            assert got[i, :len(t)].tolist() == t, f"trial {trial}: sequence {i}'s table overwritten"
+        say(f"  trial {trial}: first step's block tables intact")
+        del m2, bt_a
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16-mfma", "f32-generic"])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_prefill_skips_sequence_outside_total_q(cuda, dtype, paged):
+    say(f"[gpu] prefill: a sequence whose cu_seqlens overrun total_q is skipped ({dtype}, paged={paged})")
+    hq, hkv, d, bs = 8, 4, 128, 16
+    total, n0 = 200, 100
+    gen = torch.Generator().manual_seed(11)
+    q = torch.randn(total, hq, d, generator=gen).to(dtype)
+    k = torch.randn(total, hkv, d, generator=gen).to(dtype)
+    v = torch.randn(total, hkv, d, generator=gen).to(dtype)
+    # sequence 1 claims rows [100, 230) of a 200-row batch
+    cu = torch.tensor([0, n0, n0 + 130], dtype=torch.int32, device="cuda")
+    sentinel = 7.0
+    out = torch.full((total, hq, d), sentinel, dtype=dtype, device="cuda")
+    scale = d ** -0.5
+    if paged:
+        nb = 2 * (-(-230 // bs)) + 2
+        kc = torch.zeros(nb, bs, hkv, d, dtype=dtype)
+        vc = torch.zeros(nb, bs, hkv, d, dtype=dtype)
+        kc.view(-1, hkv, d)[:n0] = k[:n0]
+        vc.view(-1, hkv, d)[:n0] = v[:n0]
+        w = -(-230 // bs)
+        tables = torch.full((2, w), -1, dtype=torch.int32)
+        tables[0, :-(-n0 // bs)] = torch.arange(-(-n0 // bs), dtype=torch.int32)
+        tables[1] = torch.arange(w, 2 * w, dtype=torch.int32)
+        pkv.prefill_attention_varlen(q.cuda(), cu, cu, 130, 130, scale, k_cache=kc.cuda(),
+                                     v_cache=vc.cuda(), block_tables=tables.cuda(), out=out)
+    else:
+        pkv.prefill_attention_varlen(q.cuda(), cu, cu, 130, 130, scale, k=k.cuda(), v=v.cuda(), out=out)
+    torch.cuda.synchronize()
+    want = oracle.attention(q[:n0], [n0], [n0], hkv, scale, k=k[:n0], v=v[:n0])
+    err = max_abs_err(out[:n0], want)
+    bar = 2e-2 if dtype == torch.bfloat16 else 1e-4
+    say(f"  sequence 0: max |err| = {err:.3e}")
+    assert err <= bar
+    assert bool((out[n0:].float() == sentinel).all()), "rows of the skipped sequence were written"

@@ -373,9 +373,6 @@ def test_block_manager_prefix_reuse_end_to_end(cuda):
     assert err <= 2e-2
 
 
-@pytest.mark.skip(reason="a GPU run that included this test (with an experimental prefill "
-                         "variant, since removed) faulted the card and its cause could not be "
-                         "shown on the CPU; kept off the GPU until it is")
 def test_mixed_step_split_matches_one_varlen_call(cuda):
     say("[gpu] preset 7: decode rows through the decode kernel + chunks through varlen")
     from paged_kv_cache_125_amd.step import decode_rows_first, run_mixed_step
