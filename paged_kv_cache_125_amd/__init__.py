@@ -155,6 +155,18 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _used_on(stream, *tensors: Optional[torch.Tensor]) -> None:
+    """Device tensors the binding allocated itself (on the current stream)
+    and handed to kernels queued on another ``stream``: tell torch's caching
+    allocator, so that their memory is not given out again before that
+    stream's work has run."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _token_stride(t: torch.Tensor) -> int:
     # [tokens, heads, d] with each token's heads*d elements contiguous
     if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
@@ -306,7 +318,8 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
     """pkv_prefill_attention_varlen. Keys from k/v, or from the caches through
     block_tables when given."""
     total_q, hq, d = q.shape
-    if out is None:
+    own_out = out is None
+    if own_out:
         out = torch.empty((total_q, hq, d), dtype=q.dtype, device=q.device)
     num_seqs = int(cu_seqlens_q.numel()) - 1
     if block_tables is not None:
@@ -326,6 +339,8 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
         _ptr(block_tables), maxb, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, total_q,
         int(max_seqlen_q), int(max_seqlen_k), nb, bs, hq, hkv, d, float(scale), _dtype_code(q),
         _ptr(out), _stream(stream)))
+    if own_out:
+        _used_on(stream, out)
     return out
 
 
@@ -355,7 +370,8 @@ def decode_attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     through torch when not given."""
     B, hq, d = q.shape
     nb, bs, hkv, _ = k_cache.shape
-    if out is None:
+    own_out, own_ws = out is None, workspace is None
+    if own_out:
         out = torch.empty((B, hq, d), dtype=q.dtype, device=q.device)
     need = decode_workspace_bytes(B, max_context_len, hq, hkv, d, bs, q.dtype, partition_size)
     if workspace is None and need > 0:
@@ -366,6 +382,7 @@ def decode_attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         int(block_tables.shape[1]), _ptr(context_lens), B, int(max_context_len), nb, bs, hq, hkv, d,
         float(scale), _dtype_code(q), _ptr(out), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    _used_on(stream, out if own_out else None, workspace if own_ws else None)
     return out
 
 
@@ -460,7 +477,8 @@ def _pack(prefill: bool, seq_lens, num_cached, block_tables, block_size: int, de
     if device is None or torch.device(device).type == "cpu":
         dev = host
     else:
-        if dev_buffer is None:
+        own_dev = dev_buffer is None
+        if own_dev:
             dev = torch.empty(nbytes, dtype=torch.uint8, device=device)
         else:
             if dev_buffer.dtype != torch.uint8 or dev_buffer.device.type != "cuda" \
@@ -470,6 +488,8 @@ def _pack(prefill: bool, seq_lens, num_cached, block_tables, block_size: int, de
         _check(L.pkv_upload(P(host.data_ptr()), P(dev.data_ptr()), nbytes, _stream(stream)))
         if host_buffer is None:
             _hold_until_uploaded(host, stream)
+        if own_dev:
+            _used_on(stream, dev)
     res = _views(layout, dev)
     res["host_buffer"] = host
     res["layout"] = layout

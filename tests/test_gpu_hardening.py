@@ -1,4 +1,4 @@
-"""Regression tests for two ways bad step metadata could reach the kernels.
+"""Regression tests for memory the binding allocates and for bad step metadata.
 
 1. Staging lifetime. The binding packs a step's metadata into a pinned host
    buffer and uploads it with pkv_upload (hipMemcpyAsync). When the binding
@@ -10,9 +10,14 @@
 2. Prefill bounds. The prefill kernels index q, out and contiguous k/v rows
    with cu_seqlens read on the device. A sequence whose rows do not fit in
    [0, total_q) is now skipped instead of read and written out of range.
+3. Other streams. Device memory the binding allocates (decode workspace, out,
+   packed metadata) comes from torch's caching allocator on the current
+   stream. When the kernels go to another stream, the binding records the
+   tensors on it, so that the allocator does not hand that memory to the
+   current stream's next allocation before the kernels have run.
 
-Only packs, uploads, a spin kernel and prefill calls whose out-of-range rows
-stay inside the same small tensors run here."""
+Only packs, uploads, spin kernels, decode calls on valid inputs and prefill
+calls whose out-of-range rows stay inside the same small tensors run here."""
 import numpy as np
 import pytest
 import torch
@@ -88,3 +93,36 @@ def test_prefill_skips_sequence_outside_total_q(cuda, dtype, paged):
     say(f"  sequence 0: max |err| = {err:.3e}")
     assert err <= bar
     assert bool((out[n0:].float() == sentinel).all()), "rows of the skipped sequence were written"
+
+
+def test_binding_allocations_survive_work_on_another_stream(cuda):
+    say("[gpu] decode on a side stream: the binding's workspace is not reused before it has run")
+    bs, hq, hkv, d, B = 16, 8, 4, 128, 8
+    lens = [300 + 37 * i for i in range(B)]
+    counts = [-(-n // bs) for n in lens]
+    tables, at = [], 0
+    for c in counts:
+        tables.append(list(range(at, at + c)))
+        at += c
+    gen = torch.Generator().manual_seed(21)
+    kc = torch.randn(at, bs, hkv, d, generator=gen).to(torch.bfloat16).cuda()
+    vc = torch.randn(at, bs, hkv, d, generator=gen).to(torch.bfloat16).cuda()
+    q = torch.randn(B, hq, d, generator=gen).to(torch.bfloat16).cuda()
+    meta = pkv.pack_decode(lens, tables, bs, device="cuda")
+    args = (q, kc, vc, meta["block_tables"], meta["context_lens"], max(lens), d ** -0.5)
+    need = pkv.decode_workspace_bytes(B, max(lens), hq, hkv, d, bs, torch.bfloat16, 64)
+    assert need > 0
+    ref = pkv.decode_attention_paged(*args, partition_size=64)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for trial in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(20_000_000)      # the side stream's decode runs a few ms late
+        got = pkv.decode_attention_paged(*args, partition_size=64, stream=side)
+        # the current stream allocates and overwrites memory of the workspace's size at once
+        junk = [torch.empty(need, dtype=torch.uint8, device="cuda").fill_(255) for _ in range(4)]
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"trial {trial}: side-stream decode differs"
+        say(f"  trial {trial}: side-stream decode identical to the current-stream one")
+        del junk, got
