@@ -250,16 +250,30 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) st[rb][mt][r] = 0.f;
+            // The two key halves' chains alternate, and the K operand reads
+            // run kLook ahead of the MFMAs that use them: left to itself the
+            // scheduler reused one register group per step and waited out the
+            // LDS latency before every MFMA pair.
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
+                for (int mt = 0; mt < 2; ++mt) {
                     const bf16x8 kab = __builtin_bit_cast(bf16x8,
                         *reinterpret_cast<const u32x4 *>(Ks + 32 * 256 * mt + koff[kk]));
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
                         st[rb][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kab, qb[rb][kk], st[rb][mt], 0, 0, 0);
                 }
+            if constexpr (RB == 1) {
+                constexpr int kLook = 6;
+                __builtin_amdgcn_sched_group_barrier(0x100, kLook, 0);   // the first K reads
+#pragma unroll
+                for (int i = 0; i < 16 - kLook; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the next read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, kLook, 0);   // the last MFMAs
+            }
             // Online softmax: causal mask (diagonal tiles only), max on raw
             // scores, one lazy-rescale decision for both row blocks, then
             // p = exp2(q.k * c - m * c) rounded to bf16 and row sums of the
