@@ -168,7 +168,9 @@ int pkv_prefill_attention_varlen(const void *q, int64_t q_token_stride, const vo
  *  block_tables    device int32 [num_seqs, max_blocks_per_seq], -1 padded.
  *  context_lens    device int32 [num_seqs].
  *  max_context_len host upper bound of context_lens (sizes the grid and the
- *                  workspace).
+ *                  workspace). The kernels read each context length as
+ *                  min(max(context_lens[b], 0), max_context_len): a longer
+ *                  context is cut to its first max_context_len positions.
  * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128}, a positive
  * finite scale, and block_size a power of two in [1, 1024]. */
 int pkv_decode_attention_paged(const void *q, int64_t q_token_stride, const void *k_cache,

@@ -303,6 +303,7 @@ extern "C" int pkv_decode_attention_paged(
     a.bt = block_tables;
     a.maxb = max_blocks_per_seq;
     a.ctx = context_lens;
+    a.ctx_cap = max_context_len;
     a.num_seqs = num_seqs;
     a.num_blocks = num_blocks;
     a.bs = block_size;

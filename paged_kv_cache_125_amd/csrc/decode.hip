@@ -32,6 +32,14 @@
 
 namespace pkv {
 
+// A sequence's context length as the kernels use it: clamped to [0,
+// max_context_len], so that a context_lens entry past the host's bound can
+// neither address partitions the workspace does not hold nor overflow the
+// balanced split's chunk count.
+__device__ __forceinline__ int dec_ctx(const DecodeArgs &a, int b) {
+    return min(max(a.ctx[b], 0), a.ctx_cap);
+}
+
 constexpr int kDecWaves = 4;    // kv heads (waves) per workgroup, MFMA kernel
 constexpr int kDecChunk = 64;   // tokens per online-softmax step, MFMA kernel
 
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_mfma_kernel(DecodeArgs 
     const int kvh = blockIdx.z * kDecWaves + wave;
     const int b = blockIdx.y, p = blockIdx.x;
     if (kvh >= a.Hkv) return;
-    const int n = a.ctx[b];
+    const int n = dec_ctx(a, b);
     const int t_begin = p * a.P;
     if (t_begin >= n && p > 0) return;
     const int nparts = (n + a.P - 1) / a.P;
@@ -276,7 +284,7 @@ void decode_blk_kernel(DecodeArgs a) {
     const int kvh = blockIdx.x * 4 + wave;
     const int p = blockIdx.y, b = blockIdx.z;
     if (kvh >= a.Hkv) return;
-    const int n = a.ctx[b];
+    const int n = dec_ctx(a, b);
     const int t_begin = p * a.P;
     if (t_begin >= n && p > 0) return;
     const int nparts = (n + a.P - 1) / a.P;
@@ -492,7 +500,7 @@ void decode_sk_kernel(DecodeArgs a) {
     int total = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int bb = b0 + lane;
-        const int n = bb < B ? sk_nch(a.ctx[bb]) : 0;
+        const int n = bb < B ? sk_nch(dec_ctx(a, bb)) : 0;
         int incl = n;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -513,7 +521,7 @@ void decode_sk_kernel(DecodeArgs a) {
         int base = 0;
         for (int b0 = 0; b0 < B; b0 += 64) {
             const int bb = b0 + lane;
-            const int ctxv = bb < B ? a.ctx[bb] : 0;
+            const int ctxv = bb < B ? dec_ctx(a, bb) : 0;
             const int n = sk_nch(ctxv);
             int incl = n;
 #pragma unroll
@@ -548,7 +556,7 @@ void decode_sk_kernel(DecodeArgs a) {
                 u.kvh = 0;
                 do {
                     ++u.b;
-                    u.ctx = u.b < B ? a.ctx[u.b] : 0;
+                    u.ctx = u.b < B ? dec_ctx(a, u.b) : 0;
                 } while (u.b < B && u.ctx == 0);
             }
         }
@@ -784,7 +792,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int kvh = h / a.group;
-    const int n = a.ctx[b];
+    const int n = dec_ctx(a, b);
     const int t_begin = p * a.P;
     if (t_begin >= n && p > 0) return;
     const int nparts = (n + a.P - 1) / a.P;
@@ -848,7 +856,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = blockIdx.x * 4 + wave, b = blockIdx.y;
     if (h >= a.Hq) return;
-    const int n = a.ctx[b];
+    const int n = dec_ctx(a, b);
     const int nparts = (n + a.P - 1) / a.P;
     if (nparts <= 1) return;
     const int64_t pstride = (int64_t)a.Hq;
@@ -904,7 +912,7 @@ __global__ __launch_bounds__(256) void decode_sk_reduce_kernel(DecodeArgs a) {
     const int h = blockIdx.x * 4 + wave, b = blockIdx.y;
     if (h >= a.Hq) return;
     const int kvh = h / G, r = h - kvh * G;
-    const int nch = sk_nch(a.ctx[b]);
+    const int nch = sk_nch(dec_ctx(a, b));
     uint16_t *out = (uint16_t *)a.out + ((int64_t)b * a.Hq + h) * D;
     if (nch == 0) {
         *reinterpret_cast<uint32_t *>(out + lane * EPL) = 0u;
@@ -1003,7 +1011,10 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t max_ctx, int32_t Hq, int32_t Hk
                        int32_t bs, int dtype, int32_t partition_size) {
     DecodePlan p{};
     const int32_t group = Hkv > 0 ? Hq / Hkv : 1;
-    p.balanced = partition_size == 0 && blk_shape(dtype, d, bs, group);
+    // The balanced split counts chunks in 32-bit integers: all of them,
+    // num_seqs * Hkv * ceil(max_ctx / 64), must fit.
+    const int64_t chunks = (int64_t)num_seqs * Hkv * (((int64_t)max(max_ctx, 0) + kSkChunk - 1) / kSkChunk);
+    p.balanced = partition_size == 0 && blk_shape(dtype, d, bs, group) && chunks <= INT32_MAX;
     if (p.balanced) {
         p.waves = balanced_waves();
         p.P = 0;

@@ -44,6 +44,7 @@ struct DecodeArgs {
     const int32_t *bt;
     int32_t maxb;
     const int32_t *ctx;
+    int32_t ctx_cap;           // max_context_len: every context is read as min(max(ctx, 0), ctx_cap)
     int32_t num_seqs, num_blocks, bs, log2bs;
     int32_t Hq, Hkv, d, group;
     float scale_log2;          // scale * log2(e): scores live in the exp2 domain

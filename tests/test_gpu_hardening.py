@@ -126,3 +126,33 @@ def test_binding_allocations_survive_work_on_another_stream(cuda):
         assert torch.equal(got, ref), f"trial {trial}: side-stream decode differs"
         say(f"  trial {trial}: side-stream decode identical to the current-stream one")
         del junk, got
+
+
+@pytest.mark.parametrize("partition", [0, 64, 512], ids=["balanced", "fixed-5-parts", "fixed-1-part"])
+def test_decode_cuts_contexts_past_max_context_len(cuda, partition):
+    say(f"[gpu] decode: context_lens past max_context_len are cut to it (partition {partition})")
+    bs, hq, hkv, d = 64, 8, 4, 128
+    ctx = [1000, 200, 300, 64]
+    cap = 300
+    counts = [-(-n // bs) for n in ctx]
+    tables, at = [], 0
+    for c in counts:
+        tables.append(list(range(at, at + c)))
+        at += c
+    gen = torch.Generator().manual_seed(33)
+    kc = torch.randn(at, bs, hkv, d, generator=gen).to(torch.bfloat16)
+    vc = torch.randn(at, bs, hkv, d, generator=gen).to(torch.bfloat16)
+    q = torch.randn(len(ctx), hq, d, generator=gen).to(torch.bfloat16)
+    meta = pkv.pack_decode(ctx, tables, bs, device="cuda")
+    scale = d ** -0.5
+    want_part = pkv.decode_partition_size(len(ctx), cap, hq, hkv, d, bs, torch.bfloat16, partition)
+    say(f"  plan: partition size {want_part} ({'balanced' if want_part == 0 else 'fixed'})")
+    out = pkv.decode_attention_paged(q.cuda(), kc.cuda(), vc.cuda(), meta["block_tables"],
+                                     meta["context_lens"], cap, scale, partition_size=partition)
+    torch.cuda.synchronize()
+    cut = [min(n, cap) for n in ctx]
+    want = oracle.attention(q, [1] * len(ctx), cut, hkv, scale, k_cache=kc, v_cache=vc,
+                            tables=tables, block_size=bs)
+    err = max_abs_err(out, want)
+    say(f"  max |err| against the oracle on the cut contexts = {err:.3e}")
+    assert err <= 2e-2
