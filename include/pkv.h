@@ -123,7 +123,9 @@ int pkv_store_kvcache(const void *k, const void *v, int64_t k_token_stride,
  *  cu_seqlens_q/_k device int32 [num_seqs + 1], prefix sums starting at 0.
  *                  The kernels never touch q or out rows outside [0, total_q),
  *                  nor contiguous k/v rows outside it: a sequence whose range
- *                  does not fit is skipped (its out rows are left unwritten).
+ *                  does not fit, or whose key count lies outside
+ *                  [Lq_s, max_seqlen_k], is skipped (its out rows are left
+ *                  unwritten).
  *  max_seqlen_q/_k host upper bounds of Lq_s / Lk_s (size the launch grid).
  *  dtype           PKV_BF16 (MFMA path for head_dim 128) or PKV_F32.
  * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128}, a

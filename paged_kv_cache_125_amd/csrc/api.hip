@@ -246,6 +246,7 @@ extern "C" int pkv_prefill_attention_varlen(
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out = out;
     a.max_seqlen_q = max_seqlen_q;
+    a.max_seqlen_k = max_seqlen_k;
     a.total_q = total_q;
     return launched(pkv::launch_prefill(a, dtype, (hipStream_t)stream), fn);
 }

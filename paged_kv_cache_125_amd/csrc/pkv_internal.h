@@ -85,6 +85,7 @@ struct PrefillArgs {
     float scale_log2;
     void *out;
     int32_t max_seqlen_q;
+    int32_t max_seqlen_k;      // a sequence with more keys (or fewer than its queries) is skipped
     int32_t total_q;           // rows of q and out; a sequence outside them is skipped
 };
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);

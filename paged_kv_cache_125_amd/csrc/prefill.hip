@@ -107,7 +107,10 @@ void prefill_mfma_kernel(PrefillArgs a) {
     if (q0 >= Lq || q_start < 0 || q_start > a.total_q - Lq) return;
     const int k_start = a.cu_k[s];
     const int Lk = a.cu_k[s + 1] - k_start;
-    // Contiguous keys are this call's rows (Lk == Lq), so they too lie in [0, total_q).
+    // Keys must number between Lq and the host's max_seqlen_k (which bounds
+    // the work), and contiguous keys are this call's rows (Lk == Lq), so they
+    // too lie in [0, total_q).
+    if (Lk < Lq || Lk > a.max_seqlen_k) return;
     if (SRC == kContiguous && (k_start < 0 || k_start > a.total_q - Lk)) return;
     const int off = Lk - Lq;
     const int r32 = lane & 31, j = lane >> 5;
@@ -456,6 +459,7 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a) {
     if (row >= Lq || q_start < 0 || q_start > a.total_q - Lq) return;
     const int k_start = a.cu_k[s];
     const int Lk = a.cu_k[s + 1] - k_start;
+    if (Lk < Lq || Lk > a.max_seqlen_k) return;
     if (!a.paged && (k_start < 0 || k_start > a.total_q - Lk)) return;
     const int pos = Lk - Lq + row;
     const int kvh = h / a.group;

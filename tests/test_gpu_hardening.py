@@ -156,3 +156,34 @@ def test_decode_cuts_contexts_past_max_context_len(cuda, partition):
     err = max_abs_err(out, want)
     say(f"  max |err| against the oracle on the cut contexts = {err:.3e}")
     assert err <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16-mfma", "f32-generic"])
+@pytest.mark.parametrize("lk1", [5000, 50], ids=["keys-past-max_seqlen_k", "fewer-keys-than-queries"])
+def test_prefill_skips_sequence_with_key_count_out_of_range(cuda, dtype, lk1):
+    say(f"[gpu] prefill: a sequence claiming {lk1} keys for 100 queries (max_seqlen_k 100) is skipped")
+    hq, hkv, d, bs = 8, 4, 128, 16
+    n0 = 100
+    gen = torch.Generator().manual_seed(13)
+    q = torch.randn(2 * n0, hq, d, generator=gen).to(dtype)
+    k = torch.randn(n0, hkv, d, generator=gen).to(dtype)
+    v = torch.randn(n0, hkv, d, generator=gen).to(dtype)
+    nb = -(-n0 // bs)
+    kc = torch.zeros(2 * nb, bs, hkv, d, dtype=dtype)
+    vc = torch.zeros(2 * nb, bs, hkv, d, dtype=dtype)
+    kc.view(-1, hkv, d)[:n0] = k
+    vc.view(-1, hkv, d)[:n0] = v
+    tables = torch.stack([torch.arange(nb, dtype=torch.int32), torch.arange(nb, 2 * nb, dtype=torch.int32)])
+    cu_q = torch.tensor([0, n0, 2 * n0], dtype=torch.int32, device="cuda")
+    cu_k = torch.tensor([0, n0, n0 + lk1], dtype=torch.int32, device="cuda")
+    sentinel = 7.0
+    out = torch.full((2 * n0, hq, d), sentinel, dtype=dtype, device="cuda")
+    scale = d ** -0.5
+    pkv.prefill_attention_varlen(q.cuda(), cu_q, cu_k, n0, n0, scale, k_cache=kc.cuda(), v_cache=vc.cuda(),
+                                 block_tables=tables.cuda(), out=out)
+    torch.cuda.synchronize()
+    want = oracle.attention(q[:n0], [n0], [n0], hkv, scale, k=k, v=v)
+    err = max_abs_err(out[:n0], want)
+    say(f"  sequence 0: max |err| = {err:.3e}")
+    assert err <= (2e-2 if dtype == torch.bfloat16 else 1e-4)
+    assert bool((out[n0:].float() == sentinel).all()), "rows of the skipped sequence were written"
