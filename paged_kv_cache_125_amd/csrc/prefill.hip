@@ -87,18 +87,37 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // each XCD has its own L2. Work is grouped by (sequence, kv head) pair,
     // the unit that shares K and V; pair pi runs on XCD pi % 8, so all query
     // blocks and all query heads of that kv head read their K/V tiles through
-    // one L2. Within a pair: the last (longest) query blocks first, the
-    // group's heads side by side.
+    // one L2. Two orders within an XCD, chosen from the batch's K/V bytes
+    // (every workgroup reads the same count, so all agree):
+    //  - K/V within half the 256 MB MALL: longest first across all the XCD's
+    //    pairs (query-block rank major), so the tail holds only short blocks;
+    //  - larger: pair by pair, each pair's longest blocks first, so only a few
+    //    pairs' K/V are live at a time.
+    // Either way the group's heads sit side by side and every (pair, query
+    // block, head) is visited once.
     const int qblocks = (a.max_seqlen_q + BM - 1) / BM;
-    const int per_pair = qblocks * a.group;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    const int lp = local / per_pair, within = local - lp * per_pair;
+    const int64_t kv_bytes = (int64_t)a.cu_k[a.num_seqs] * a.Hkv * kPfD * 2 * 2;
+    int lp, rank, head;
+    if (kv_bytes <= (int64_t(128) << 20)) {
+        const int per_rank = ((a.num_seqs * a.Hkv + 7) / 8) * a.group;
+        rank = local / per_rank;
+        const int within = local - rank * per_rank;
+        lp = within / a.group;
+        head = within - lp * a.group;
+    } else {
+        const int per_pair = qblocks * a.group;
+        lp = local / per_pair;
+        const int within = local - lp * per_pair;
+        rank = within / a.group;
+        head = within - rank * a.group;
+    }
     const int pair = 8 * lp + xcd;
     if (pair >= a.num_seqs * a.Hkv) return;
     const int s = pair / a.Hkv;
     const int kvh = pair - s * a.Hkv;
-    const int qt = qblocks - 1 - within / a.group;
-    const int h = kvh * a.group + (within - (within / a.group) * a.group);
+    const int qt = qblocks - 1 - rank;
+    const int h = kvh * a.group + head;
     const int q_start = a.cu_q[s];
     const int Lq = a.cu_q[s + 1] - q_start;
     const int q0 = qt * BM;
