@@ -248,6 +248,13 @@ extern "C" int pkv_prefill_attention_varlen(
     a.max_seqlen_q = max_seqlen_q;
     a.max_seqlen_k = max_seqlen_k;
     a.total_q = total_q;
+    // Longest query blocks first across pairs when the batch's K/V fits in half
+    // the 256 MB MALL: contiguous keys are the call's own rows, paged keys are
+    // bounded by num_seqs * max_seqlen_k.
+    {
+        const int64_t keys = a.paged ? (int64_t)num_seqs * max_seqlen_k : (int64_t)total_q;
+        a.by_rank = keys * num_kv_heads * head_dim * 2 * 2 <= (int64_t(128) << 20);
+    }
     return launched(pkv::launch_prefill(a, dtype, (hipStream_t)stream), fn);
 }
 

@@ -87,6 +87,7 @@ struct PrefillArgs {
     int32_t max_seqlen_q;
     int32_t max_seqlen_k;      // a sequence with more keys (or fewer than its queries) is skipped
     int32_t total_q;           // rows of q and out; a sequence outside them is skipped
+    int32_t by_rank;           // grid order: longest query blocks first across pairs (set by the host)
 };
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);
 

@@ -87,8 +87,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // each XCD has its own L2. Work is grouped by (sequence, kv head) pair,
     // the unit that shares K and V; pair pi runs on XCD pi % 8, so all query
     // blocks and all query heads of that kv head read their K/V tiles through
-    // one L2. Two orders within an XCD, chosen from the batch's K/V bytes
-    // (every workgroup reads the same count, so all agree):
+    // one L2. Two orders within an XCD, chosen on the host from the batch's
+    // K/V bytes (a bound on them when the keys come through block tables):
     //  - K/V within half the 256 MB MALL: longest first across all the XCD's
     //    pairs (query-block rank major), so the tail holds only short blocks;
     //  - larger: pair by pair, each pair's longest blocks first, so only a few
@@ -97,9 +97,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // block, head) is visited once.
     const int qblocks = (a.max_seqlen_q + BM - 1) / BM;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    const int64_t kv_bytes = (int64_t)a.cu_k[a.num_seqs] * a.Hkv * kPfD * 2 * 2;
     int lp, rank, head;
-    if (kv_bytes <= (int64_t(128) << 20)) {
+    if (a.by_rank) {
         const int per_rank = ((a.num_seqs * a.Hkv + 7) / 8) * a.group;
         rank = local / per_rank;
         const int within = local - rank * per_rank;
@@ -118,19 +117,21 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int kvh = pair - s * a.Hkv;
     const int qt = qblocks - 1 - rank;
     const int h = kvh * a.group + head;
-    const int q_start = a.cu_q[s];
-    const int Lq = a.cu_q[s + 1] - q_start;
+    // All four bounds in one round trip (a workgroup with no rows here
+    // learns it from the first two and leaves).
+    const int q_start = a.cu_q[s], q_end = a.cu_q[s + 1];
+    const int k_start = a.cu_k[s], k_end = a.cu_k[s + 1];
+    const int Lq = q_end - q_start, Lk = k_end - k_start;
     const int q0 = qt * BM;
-    // Rows outside [0, total_q) of q and out are never touched, whatever
-    // cu_seqlens_q holds.
-    if (q0 >= Lq || q_start < 0 || q_start > a.total_q - Lq) return;
-    const int k_start = a.cu_k[s];
-    const int Lk = a.cu_k[s + 1] - k_start;
-    // Keys must number between Lq and the host's max_seqlen_k (which bounds
-    // the work), and contiguous keys are this call's rows (Lk == Lq), so they
-    // too lie in [0, total_q).
-    if (Lk < Lq || Lk > a.max_seqlen_k) return;
-    if (SRC == kContiguous && (k_start < 0 || k_start > a.total_q - Lk)) return;
+    // One test, so that the four loads above issue together. Rows outside
+    // [0, total_q) of q and out are never touched, whatever cu_seqlens_q
+    // holds; keys must number between Lq and the host's max_seqlen_k (which
+    // bounds the work); contiguous keys are this call's rows (Lk == Lq), so
+    // they too lie in [0, total_q).
+    const bool skip = (q0 >= Lq) | (q_start < 0) | (q_start > a.total_q - Lq) | (Lk < Lq) |
+                      (Lk > a.max_seqlen_k) |
+                      (SRC == kContiguous && ((k_start < 0) | (k_start > a.total_q - Lk)));
+    if (skip) return;
     const int off = Lk - Lq;
     const int r32 = lane & 31, j = lane >> 5;
     // The wave owns rows q0 + 32*RB*wave + 32*rb + r32, rb < RB.
