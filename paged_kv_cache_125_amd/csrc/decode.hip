@@ -13,6 +13,11 @@
 // Gimelshein 2018). A sequence that fits one partition is finished in place.
 //
 // Kernels:
+//  decode_sk_kernel<G> + decode_sk_reduce_kernel<G>   the default for bf16,
+//      head_dim 128, block size a multiple of 64: the (sequence, kv head,
+//      64-position chunk) work list split evenly over one wave per SIMD
+//      (stream-K), partials only where a wave's range cuts a segment, and
+//      their combine. Used whenever no partition size is forced.
 //  decode_blk_kernel<G, CH>       bf16, head_dim 128, block size a multiple of
 //      CH (nano-vLLM's 256 included), G <= 16: both contractions on MFMA,
 //      buffer loads range-checked by the hardware (see below).
@@ -25,6 +30,8 @@
 //  decode_generic_kernel<T, D>    any dtype/group, fp32 math, one wave per
 //      (sequence, q head, partition); used for fp32 and small head dims.
 //  decode_reduce_kernel<T>        the log-sum-exp combine of partitions.
+// The fixed-partition kernels above serve forced partition sizes and the
+// shapes outside the default kernel's range.
 #include <stdlib.h>
 
 #include "pkv_device.h"
