@@ -160,6 +160,24 @@ def test_decode_workspace_and_partition():
     assert pkv.decode_partition_size(4, 100, 4, 2, 64, 16, torch.float32, 48) == 48
 
 
+def test_balanced_decode_split_only_while_its_chunk_count_fits_32_bits():
+    # the balanced split counts num_seqs * Hkv * ceil(max_context_len / 64) chunks in
+    # 32-bit integers; past that the plan falls back to fixed partitions, and the
+    # workspace query follows the same plan
+    limit = 2 ** 31 - 1
+    fits = limit // (8 * 64)            # sequences at Hkv 8 and 4096 positions (64 chunks each)
+    assert pkv.decode_partition_size(fits, 4096, 16, 8, 128, 256, torch.bfloat16) == 0
+    assert pkv.decode_partition_size(fits + 1, 4096, 16, 8, 128, 256, torch.bfloat16) > 0
+    big = 2 ** 30                       # one sequence's bound alone: 8 * 2^24 chunks fit ...
+    assert pkv.decode_partition_size(1, big, 16, 8, 128, 256, torch.bfloat16) == 0
+    # ... sixteen such sequences do not
+    P = pkv.decode_partition_size(16, big, 16, 8, 128, 256, torch.bfloat16)
+    assert P > 0
+    n = pkv.decode_workspace_bytes(16, big, 16, 8, 128, 256, torch.bfloat16)
+    parts = -(-big // P)
+    assert n >= 16 * parts * 16 * 128 * 4      # room for every planned partition's partial
+
+
 def test_rope_table_and_argument_checks():
     t = pkv.rope_cos_sin_table(9, 8, 10000.0, device="cpu")
     p = np.arange(9)[:, None] * np.power(10000.0, -np.arange(4) * 2.0 / 8)[None, :]
