@@ -478,6 +478,14 @@ __device__ __forceinline__ int sk_nch(int ctx) { return (ctx + kSkChunk - 1) / k
 // The wave whose range holds chunk x, and where wave w's range starts.
 __device__ __forceinline__ int64_t sk_owner(int64_t x, int64_t C, int64_t W) { return ((x + 1) * W - 1) / C; }
 __device__ __forceinline__ int64_t sk_start(int64_t w, int64_t C, int64_t W) { return w * C / W; }
+// Waves the split uses out of the W launched: all of them while each gets at
+// least kSkMinChunks chunks, fewer for a small batch, so that a segment spans
+// fewer waves and the combine gathers fewer partials. Both kernels derive it
+// from the same chunk count.
+constexpr int kSkMinChunks = 2;
+__device__ __forceinline__ int64_t sk_waves(int64_t C, int64_t W) {
+    return max((int64_t)1, min(W, C / kSkMinChunks));
+}
 
 // Position of one chunk in the work list (all wave-uniform).
 struct SkCursor {
@@ -519,7 +527,9 @@ void decode_sk_kernel(DecodeArgs a) {
     }
     if (w == 0 && lane == 0) a.ws_cum[B] = total;
     const int64_t C = (int64_t)Hkv * total;
-    const int64_t x0 = sk_start(w, C, W), x1 = sk_start(w + 1, C, W);
+    const int64_t We = sk_waves(C, W);
+    if (w >= We) return;
+    const int64_t x0 = sk_start(w, C, We), x1 = sk_start(w + 1, C, We);
     if (x0 >= x1) return;
 
     // Locate chunk x0: the sequence b with Hkv*cum_b <= x0 < Hkv*cum_(b+1).
@@ -925,8 +935,8 @@ __global__ __launch_bounds__(256) void decode_sk_reduce_kernel(DecodeArgs a) {
         *reinterpret_cast<uint32_t *>(out + lane * EPL) = 0u;
         return;
     }
-    const int64_t W = a.waves;
     const int64_t C = (int64_t)a.Hkv * a.ws_cum[a.num_seqs];
+    const int64_t W = sk_waves(C, a.waves);
     const int64_t g0 = (int64_t)a.Hkv * a.ws_cum[b] + (int64_t)kvh * nch;
     const int64_t wf = sk_owner(g0, C, W), wl = sk_owner(g0 + nch - 1, C, W);
     if (wf == wl) return;
@@ -950,14 +960,36 @@ __global__ __launch_bounds__(256) void decode_sk_reduce_kernel(DecodeArgs a) {
         const bool ok = holds(i);
         const float wgt = ok ? fast_exp2(a.ws_ml[slot_of(i) * 2] - M) : 0.f;
         if (ok) den = fmaf(wgt, a.ws_ml[slot_of(i) * 2 + 1], den);
-        const uint64_t live = __builtin_amdgcn_ballot_w64(ok);
-        const int cnt = min(64, n - i0);
-        for (int k = 0; k < cnt; ++k) {
-            if (!((live >> k) & 1)) continue;
-            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
-            const float *acc = a.ws_acc + slot_of(i0 + k) * D + lane * EPL;
-            o0 = fmaf(wk, acc[0], o0);
-            o1 = fmaf(wk, acc[1], o1);
+        // Up to 16 live candidates at a time, their accumulator rows loaded
+        // together: one round trip per 16 partials instead of one per partial
+        // (a small batch spreads one segment over many waves).
+        uint64_t live = __builtin_amdgcn_ballot_w64(ok);
+        while (live) {
+            constexpr int kBatch = 16;
+            int kk[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                kk[u] = live ? (int)__builtin_ctzll(live) : -1;
+                live &= live - 1;
+            }
+            float v0[kBatch], v1[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                v0[u] = 0.f;
+                v1[u] = 0.f;
+                if (kk[u] >= 0) {
+                    const float *acc = a.ws_acc + slot_of(i0 + kk[u]) * D + lane * EPL;
+                    v0[u] = acc[0];
+                    v1[u] = acc[1];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (kk[u] < 0) continue;
+                const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), kk[u]));
+                o0 = fmaf(wk, v0[u], o0);
+                o1 = fmaf(wk, v1[u], o1);
+            }
         }
     }
     den = wave_sum(den);
