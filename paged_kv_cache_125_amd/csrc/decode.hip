@@ -34,6 +34,8 @@
 // shapes outside the default kernel's range.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -960,17 +962,17 @@ __global__ __launch_bounds__(256) void decode_sk_reduce_kernel(DecodeArgs a) {
         const bool ok = holds(i);
         const float wgt = ok ? fast_exp2(a.ws_ml[slot_of(i) * 2] - M) : 0.f;
         if (ok) den = fmaf(wgt, a.ws_ml[slot_of(i) * 2 + 1], den);
-        // Up to 16 live candidates at a time, their accumulator rows loaded
-        // together: one round trip per 16 partials instead of one per partial
-        // (a small batch spreads one segment over many waves).
-        uint64_t live = __builtin_amdgcn_ballot_w64(ok);
-        while (live) {
-            constexpr int kBatch = 16;
+        // Live candidates in batches whose accumulator rows load together: one
+        // round trip per batch instead of one per partial. A small batch spreads
+        // one segment over many waves (16 at a time then); otherwise a segment
+        // has a few partials (4 at a time, fewer idle slots).
+        auto gather = [&](auto width, uint64_t &lv) {
+            constexpr int kBatch = decltype(width)::value;
             int kk[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                kk[u] = live ? (int)__builtin_ctzll(live) : -1;
-                live &= live - 1;
+                kk[u] = lv ? (int)__builtin_ctzll(lv) : -1;
+                lv &= lv - 1;
             }
             float v0[kBatch], v1[kBatch];
 #pragma unroll
@@ -990,6 +992,12 @@ __global__ __launch_bounds__(256) void decode_sk_reduce_kernel(DecodeArgs a) {
                 o0 = fmaf(wk, v0[u], o0);
                 o1 = fmaf(wk, v1[u], o1);
             }
+        };
+        uint64_t live = __builtin_amdgcn_ballot_w64(ok);
+        if (__builtin_popcountll(live) <= 4) {
+            gather(std::integral_constant<int, 4>{}, live);
+        } else {
+            while (live) gather(std::integral_constant<int, 16>{}, live);
         }
     }
     den = wave_sum(den);
