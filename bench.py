@@ -1,26 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of each of the metric's
-two workloads, inputs resident in HBM:
+One step = one pass of the whole path over one batch of each workload below,
+inputs resident in HBM. A decode workload is: pack metadata (host, one pinned
+buffer, one copy) -> store_kvcache of each sequence's new token -> paged decode
+attention with the split over all waves and its combine. A prefill workload
+is: pack -> store_kvcache of every new token -> varlen causal prefill
+attention. The default step holds, in this order:
 
-  decode : pack metadata (host, one pinned buffer, one copy) -> store_kvcache
-           of the new token of each sequence -> paged decode attention with
-           split-context partitions and the combine. Workload: Qwen3-0.6B-
-           shaped decode (16 q / 8 kv heads, head_dim 128, block size 256,
-           64 sequences, context U{512..4096}).
-  prefill: pack -> store_kvcache of every prompt token -> varlen causal
-           prefill attention. Workload: 16 prompts U{128..2048} under a
-           16384-token budget, 16 q / 8 kv heads, head_dim 128.
+  decode  Qwen3-8B-shaped long-context decode: 32 q / 8 kv heads, head_dim
+          128, block size 256, 512 sequences, context log-uniform in
+          [256, 32768]                                      (the `value`)
+  prefill prefix-cache hits: 32 prompts of 2048 tokens, the even ones sharing
+          a cached 1024-token prefix read through the block tables, 16 q /
+          8 kv heads, head_dim 128                          (secondary)
+  decode  Qwen3-0.6B-shaped decode: 16 q / 8 kv heads, 64 sequences,
+          context U{512..4096}                              (extra part)
+  prefill varlen: 16 prompts U{128..2048} under a 16384-token budget
+                                                            (extra part)
 
-`value` is the decode attention's algorithmic HBM throughput (GB/s); the
-prefill attention's TFLOP/s is reported beside it. Each call is timed with HIP
-events on the stream it runs on. Several copies of the inputs are used in
-rotation so that no step finds its data in the 256 MB last-level cache.
+`value` is the long-context decode attention's algorithmic HBM throughput
+(GB/s); the prefix-hit prefill attention's TFLOP/s and fraction of the bf16
+MFMA peak sit beside it. Each call is timed with HIP events on the stream it
+runs on. Several copies of the inputs are used in rotation so that no step
+finds its data in the 256 MB last-level cache. A read-only streaming kernel
+(libpkv_probe) is timed on a 2 GiB buffer in the same run, as an achievable
+reference beside the published HBM peak.
 
-`--workload` selects other presets (each alone): decode-long (Qwen3-8B-shaped,
-512 sequences, log-uniform 256..32768) and prefill-prefix (32 x 2048 with a
-cached 1024-token prefix on half of them).
+`--workload` selects other combinations (see WORKLOADS).
 """
 from __future__ import annotations
 
@@ -45,7 +52,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "paged decode attn HBM GB/s (% peak) + varlen prefill attn TFLOP/s (% MFMA peak)"
 
 WORKLOADS = {
-    "default": [("decode", 2), ("prefill", 3)],
+    "default": [("decode", 5), ("prefill", 4), ("decode", 2), ("prefill", 3)],
+    "small": [("decode", 2), ("prefill", 3)],
     "decode": [("decode", 2)],
     "prefill": [("prefill", 3)],
     "decode-long": [("decode", 5)],
@@ -487,6 +495,54 @@ def device_copy_rate(reps: int = 5) -> float:
     return 2 * CALIBRATION_BYTES / sec / 1e9
 
 
+STREAM_BYTES = 2 << 30          # buffer of the read-only streaming reference
+
+
+def stream_read_rates(reps: int = 5) -> dict:
+    """GB/s of libpkv_probe's read-only streaming kernels over a 2 GiB buffer
+    of random words (8x the last-level cache, so every pass comes from HBM),
+    timed with events on the current stream: the plain grid-stride form and the
+    decode-shaped form (2 KB rows of eight 256-byte heads, one head per wave),
+    each at 4, 8 and 16 workgroups per CU, the best kept. An achievable
+    streaming-read reference beside the published 8 TB/s."""
+    import ctypes
+    from paged_kv_cache_125_amd.build import PROBE_LIB
+    L = ctypes.CDLL(PROBE_LIB)
+    L.pkv_probe_stream_read.restype = ctypes.c_int
+    L.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (STREAM_BYTES // 4,), dtype=torch.int32, device="cuda",
+                        generator=gen)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for mode, name in ((0, "plain"), (1, "decode_shaped")):
+        best = None
+        for per_cu in (4, 8, 16):
+            blocks = cus * per_cu
+            args = (ctypes.c_void_p(buf.data_ptr()), STREAM_BYTES, mode, 2048, blocks,
+                    ctypes.c_void_p(sink.data_ptr()), stream)
+            if L.pkv_probe_stream_read(*args) != 0:
+                raise RuntimeError("pkv_probe_stream_read failed")
+            e0.record()
+            for _ in range(reps):
+                L.pkv_probe_stream_read(*args)
+            e1.record()
+            torch.cuda.synchronize()
+            gbps = STREAM_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if best is None or gbps > best["GBps"]:
+                best = {"GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBS, "workgroups_per_cu": per_cu}
+        out[name] = best
+    del buf
+    torch.cuda.empty_cache()
+    out["bytes_read"] = STREAM_BYTES
+    return out
+
+
 def _source_sha(kernel_file: str) -> str:
     src = os.path.join(ROOT, "paged_kv_cache_125_amd", "csrc", kernel_file)
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -571,6 +627,54 @@ def summarize_counters(fetch_dir, write_dir, workload):
     print(json.dumps({k: data[k]["hbm_bytes_per_launch"] for k in sorted(data)}, indent=1))
 
 
+# ----------------------------------------------------------------- kernel trace
+
+# Attention kernels each part's call dispatches once per step, by phase.
+TRACE_KERNELS = {"decode": ["decode_sk_kernel", "decode_sk_reduce_kernel"],
+                 "prefill": ["prefill_mfma_kernel"]}
+
+
+def summarize_trace(trace_dir, workload, steps, warmup, command):
+    """Per-workload kernel durations from a `rocprofv3 --kernel-trace` run of
+    `bench.py --workload W --steps K --warmup W'`. The bench runs every pass
+    (warmup, wall-clock, event-timed) part by part, so the n-th dispatch of an
+    attention kernel belongs to a known part; that order is rebuilt here and
+    checked against the dispatch count. Durations of the two timed passes only
+    (warmup excluded). Prints a markdown summary."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(path)))
+    if not rows:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    parts = WORKLOADS[workload]
+    names = {2: "decode 0.6B b64", 3: "prefill varlen 16x", 4: "prefill prefix-hit 32x2048",
+             5: "decode 8B b512 long"}
+    out = [f"Command: `{command}`", "",
+           "| Kernel | Workload | Dispatches (timed) | Mean us | Median us | Min us | Max us |",
+           "|---|---|---|---|---|---|---|"]
+    for phase, kernels in TRACE_KERNELS.items():
+        mine = [p for p in parts if p[0] == phase]
+        if not mine:
+            continue
+        order = [(p, pas) for pas, n in (("warmup", warmup), ("timed", steps), ("events", steps))
+                 for p in mine for _ in range(n)]
+        for k in kernels:
+            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+                    for r in rows if r["Kernel_Name"].split("(")[0].split("<")[0].endswith(k)]
+            if not durs:
+                continue
+            if len(durs) != len(order):
+                raise SystemExit(f"{k}: {len(durs)} dispatches, expected {len(order)}")
+            for p in mine:
+                d = [t for t, (pp, pas) in zip(durs, order) if pp == p and pas != "warmup"]
+                out.append(f"| {k} | {names.get(p[1], p[1])} (preset {p[1]}) | {len(d)} | "
+                           f"{np.mean(d):.1f} | {np.median(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+    print("\n".join(out))
+
+
 # ----------------------------------------------------------------- main
 
 # Steps per chunk of the event-timed pass (see the comment there).
@@ -604,9 +708,19 @@ def main():
                     help="first run a plain 1 GiB device copy (scales the HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs into profiles/counters.json and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
+                    help="per-workload kernel durations of a rocprofv3 --kernel-trace run of "
+                         "the bench with the same --workload/--steps/--warmup, then exit")
     args = ap.parse_args()
     if args.summarize_counters:
+        if len({ph for ph, _ in WORKLOADS[args.workload]}) != len(WORKLOADS[args.workload]):
+            raise SystemExit("counter runs need a workload with one part per phase "
+                             "(the counters are averaged per kernel name)")
         summarize_counters(*args.summarize_counters, args.workload)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.workload, args.steps, args.warmup,
+                        args.summarize_trace[1])
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -628,6 +742,9 @@ def main():
 
     copy_gbps = device_copy_rate()
     log(f"[bench] 1 GiB device copy: {copy_gbps:.0f} GB/s (read + write)")
+    stream_read = stream_read_rates()
+    log(f"[bench] 2 GiB read-only stream: plain {stream_read['plain']['GBps']:.0f} GB/s, "
+        f"decode-shaped {stream_read['decode_shaped']['GBps']:.0f} GB/s")
     if args.copy_calibration:
         src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -764,13 +881,35 @@ def main():
     if args.workload == "decode-graph":
         log("[bench] 28-layer decode steps: eager vs hipGraph")
         line["decode_graph"] = decode_graph_compare()
+    sec = line["secondary"]
     if pre is not None:
-        line["secondary"]["prefill_attention_TFLOPs"] = pre["attention_TFLOPs"]
-        line["secondary"]["prefill_frac_of_mfma_peak"] = pre["attention_frac_mfma"]
+        sec["prefill_attention_TFLOPs"] = pre["attention_TFLOPs"]
+        sec["prefill_frac_of_mfma_peak"] = pre["attention_frac_mfma"]
+        sec["prefill_workload"] = names[pre["preset"]]
+        if dec is not None:
+            # the MFMA side of the step, in the same form as `roofline`
+            sec["prefill_roofline"] = {
+                "bound": "mfma", "achieved": pre["attention_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": pre["attention_frac_mfma"],
+                "traffic": counters_traffic("prefill.hip", f"prefill-preset{pre['preset']}"),
+                "kernel": "prefill_mfma_kernel", "algorithmic_flops_per_launch": pre["attention_flops"],
+                "avg_launch_us": pre["attention_us"]}
     if dec is not None:
-        line["secondary"]["decode_frac_of_hbm_peak"] = dec["attention_frac_hbm"]
-    # what a plain streaming kernel reaches on this GPU, beside the published peak
-    line["secondary"]["device_copy_GBps"] = copy_gbps
+        sec["decode_frac_of_hbm_peak"] = dec["attention_frac_hbm"]
+    # every part's attention figure, by workload
+    for sm in summaries:
+        k = names[sm["preset"]]
+        if sm["phase"] == "decode":
+            sec.setdefault("per_workload", {})[k] = {
+                "GBps": sm["attention_GBps"], "frac_of_hbm_peak": sm["attention_frac_hbm"],
+                "attention_us": sm["attention_us"]}
+        else:
+            sec.setdefault("per_workload", {})[k] = {
+                "TFLOPs": sm["attention_TFLOPs"], "frac_of_mfma_peak": sm["attention_frac_mfma"],
+                "attention_us": sm["attention_us"]}
+    # what plain streaming kernels reach on this GPU, beside the published peak
+    sec["device_copy_GBps"] = copy_gbps
+    sec["stream_read"] = stream_read
     print(json.dumps(line), flush=True)
 
 

@@ -86,7 +86,8 @@ int64_t orc_slots(int32_t n_ranges, const int32_t *rseq, const int32_t *rbegin,
     return n;
 }
 
-/* [MR] "slot_mapping 负责写入": row i of the new K (or V) is copied, bit for bit,
+/* [MR] "FlashAttention Kernel 函参准备" (slot_mapping names where each new
+ * token's K/V goes): row i of the new K (or V) is copied, bit for bit,
  * into the cache row numbered slots[i] of a cache viewed as
  * [num_blocks * block_size, row_bytes]. slots[i] < 0 is skipped.
  * Returns 0, or -1 for a slot past the pool, or -2 for a duplicate slot

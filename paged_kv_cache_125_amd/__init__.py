@@ -174,12 +174,77 @@ def _token_stride(t: torch.Tensor) -> int:
     return int(t.stride(0))
 
 
+# ----------------------------------------------------------------- validation
+# The C ABI validates sizes and alignment, but it sees only pointers: it cannot
+# tell that two tensors disagree in dtype or shape, or live on different
+# devices. A kernel then indexes with the wrong row size and leaves its
+# buffers. Every entry point below checks that its tensors agree before any C
+# call, and raises ValueError when they do not.
+
+_ATTN_DTYPES = (torch.bfloat16, torch.float32)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _one_gpu(**tensors) -> None:
+    """All given tensors on one device, and that device a GPU."""
+    devs = {name: t.device for name, t in tensors.items() if t is not None}
+    _need(len(set(devs.values())) == 1,
+          "tensors on different devices: " + ", ".join(f"{n} on {d}" for n, d in devs.items()))
+    _need(next(iter(devs.values())).type == "cuda", "the tensors must be on a GPU")
+
+
+def _int32_vec(t: torch.Tensor, name: str, min_len: int) -> None:
+    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}")
+    _need(t.dim() == 1 and t.is_contiguous(), f"{name} must be a contiguous 1-D tensor")
+    _need(t.numel() >= min_len, f"{name} has {t.numel()} entries, needs {min_len}")
+
+
+def _int32_table(t: torch.Tensor, name: str, min_rows: int) -> None:
+    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}")
+    _need(t.dim() == 2 and t.is_contiguous(), f"{name} must be a contiguous 2-D tensor")
+    _need(t.shape[0] >= min_rows and t.shape[1] >= 1,
+          f"{name} has shape {tuple(t.shape)}, needs at least {min_rows} rows")
+
+
+def _pool(k_cache: torch.Tensor, v_cache: torch.Tensor, dtype: torch.dtype) -> None:
+    _need(k_cache.dim() == 4, "caches must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    _need(k_cache.shape == v_cache.shape, "k_cache and v_cache differ in shape")
+    _need(k_cache.dtype == dtype and v_cache.dtype == dtype,
+          f"cache dtype {k_cache.dtype}/{v_cache.dtype} differs from {dtype}")
+    _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+
+
+def _rows(t: torch.Tensor, name: str, heads: int, head_dim: int, dtype: torch.dtype,
+          min_rows: int) -> None:
+    """[tokens, heads, head_dim] with contiguous rows, of the given dtype."""
+    _need(t.dtype == dtype, f"{name} dtype {t.dtype} differs from {dtype}")
+    _need(t.dim() == 3 and t.shape[1] == heads and t.shape[2] == head_dim,
+          f"{name} has shape {tuple(t.shape)}, expected [tokens, {heads}, {head_dim}]")
+    _need(t.shape[0] >= min_rows, f"{name} has {t.shape[0]} rows, needs {min_rows}")
+    _token_stride(t)
+
+
+def _out(out: torch.Tensor, like: torch.Tensor) -> None:
+    _need(out.dtype == like.dtype, f"out dtype {out.dtype} differs from q's {like.dtype}")
+    _need(tuple(out.shape) == tuple(like.shape),
+          f"out has shape {tuple(out.shape)}, expected {tuple(like.shape)}")
+    _need(out.is_contiguous(), "out must be contiguous")
+
+
 def store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   slot_mapping: torch.Tensor, stream=None) -> None:
     """pkv_store_kvcache: k/v [N, Hkv, d] -> caches [num_blocks, bs, Hkv, d] at slot_mapping."""
+    _pool(k_cache, v_cache, k_cache.dtype)
     nb, bs, hkv, d = k_cache.shape
-    if slot_mapping.dtype != torch.int32:
-        raise TypeError("slot_mapping must be int32")
+    _int32_vec(slot_mapping, "slot_mapping", 0)
+    n = int(slot_mapping.numel())
+    _rows(k, "k", hkv, d, k_cache.dtype, n)
+    _rows(v, "v", hkv, d, k_cache.dtype, n)
+    _one_gpu(k=k, v=v, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping)
     _check(lib().pkv_store_kvcache(_ptr(k), _ptr(v), _token_stride(k), _token_stride(v),
                                    _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
                                    int(slot_mapping.numel()), nb, bs, hkv, d, _dtype_code(k_cache),
@@ -292,14 +357,22 @@ def rope_store_kvcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cach
     """pkv_rope_store_kvcache: rotate q (in place) and k by ``positions``,
     store the rotated k and v into the caches at ``slot_mapping`` (and the
     rotated k back into ``k`` when ``write_k``)."""
+    _pool(k_cache, v_cache, k_cache.dtype)
     nb, bs, hkv, d = k_cache.shape
+    _need(q.dim() == 3, "q must be [tokens, num_q_heads, head_dim]")
     n, hq, _ = q.shape
-    if slot_mapping.dtype != torch.int32 or positions.dtype != torch.int32:
-        raise TypeError("slot_mapping and positions must be int32")
+    _rows(q, "q", hq, d, k_cache.dtype, n)
+    _rows(k, "k", hkv, d, k_cache.dtype, n)
+    _rows(v, "v", hkv, d, k_cache.dtype, n)
+    _need(k.shape[0] == n and v.shape[0] == n, "q, k and v must have one row per token")
+    _int32_vec(slot_mapping, "slot_mapping", n)
+    _int32_vec(positions, "positions", n)
+    _need(slot_mapping.numel() == n and positions.numel() == n,
+          "slot_mapping and positions must have one entry per token")
     if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or not cos_sin.is_contiguous():
         raise TypeError("cos_sin must be a contiguous float32 [max_positions, rot_dim] table")
-    if slot_mapping.numel() != n or positions.numel() != n or k.shape[0] != n or v.shape[0] != n:
-        raise ValueError("q, k, v, slot_mapping and positions must have one entry per token")
+    _one_gpu(q=q, k=k, v=v, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping,
+             positions=positions, cos_sin=cos_sin)
     _check(lib().pkv_rope_store_kvcache(
         _ptr(q), _token_stride(q), _ptr(k), _ptr(v), _token_stride(k), _token_stride(v),
         _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), _ptr(positions), _ptr(cos_sin),
@@ -317,23 +390,43 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
                              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """pkv_prefill_attention_varlen. Keys from k/v, or from the caches through
     block_tables when given."""
+    _need(q.dim() == 3, "q must be [tokens, num_q_heads, head_dim]")
+    _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
     total_q, hq, d = q.shape
-    own_out = out is None
-    if own_out:
-        out = torch.empty((total_q, hq, d), dtype=q.dtype, device=q.device)
+    _rows(q, "q", hq, d, q.dtype, 0)
+    _int32_vec(cu_seqlens_q, "cu_seqlens_q", 1)
+    _int32_vec(cu_seqlens_k, "cu_seqlens_k", 1)
+    _need(cu_seqlens_k.numel() == cu_seqlens_q.numel(),
+          "cu_seqlens_q and cu_seqlens_k must have one entry per sequence plus one")
     num_seqs = int(cu_seqlens_q.numel()) - 1
     if block_tables is not None:
+        _need(k_cache is not None and v_cache is not None, "block_tables need k_cache and v_cache")
+        _pool(k_cache, v_cache, q.dtype)
         nb, bs, hkv, _ = k_cache.shape
+        _need(k_cache.shape[3] == d, "cache head_dim differs from q's")
+        _int32_table(block_tables, "block_tables", num_seqs)
         maxb = int(block_tables.shape[1])
         kv_stride = 0
     else:
+        _need(k is not None and v is not None, "k and v are needed without block_tables")
         nb, bs, maxb = 0, 1, 0
+        _need(k.dim() == 3, "k must be [tokens, num_kv_heads, head_dim]")
         hkv = k.shape[1]
+        _rows(k, "k", hkv, d, q.dtype, total_q)
+        _rows(v, "v", hkv, d, q.dtype, total_q)
         kv_stride = _token_stride(k)
         if _token_stride(v) != kv_stride:
             raise ValueError("k and v must share a token stride")
     if num_kv_heads is not None and num_kv_heads != hkv:
         raise ValueError("num_kv_heads does not match the key tensors")
+    if out is not None:
+        _out(out, q)
+    _one_gpu(q=q, k=k, v=v, k_cache=k_cache if block_tables is not None else None,
+             v_cache=v_cache if block_tables is not None else None, block_tables=block_tables,
+             cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, out=out)
+    own_out = out is None
+    if own_out:
+        out = torch.empty((total_q, hq, d), dtype=q.dtype, device=q.device)
     _check(lib().pkv_prefill_attention_varlen(
         _ptr(q), _token_stride(q), _ptr(k), _ptr(v), kv_stride, _ptr(k_cache), _ptr(v_cache),
         _ptr(block_tables), maxb, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, total_q,
@@ -368,8 +461,22 @@ def decode_attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     """pkv_decode_attention_paged: q [B, Hq, d] against context_lens keys per
     sequence. ``workspace`` (uint8, >= decode_workspace_bytes) is allocated
     through torch when not given."""
+    _need(q.dim() == 3, "q must be [num_seqs, num_q_heads, head_dim]")
+    _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
     B, hq, d = q.shape
+    _rows(q, "q", hq, d, q.dtype, 0)
+    _pool(k_cache, v_cache, q.dtype)
     nb, bs, hkv, _ = k_cache.shape
+    _need(k_cache.shape[3] == d, "cache head_dim differs from q's")
+    _int32_table(block_tables, "block_tables", B)
+    _int32_vec(context_lens, "context_lens", B)
+    if out is not None:
+        _out(out, q)
+    if workspace is not None:
+        _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(),
+              "workspace must be a contiguous uint8 tensor")
+    _one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+             context_lens=context_lens, out=out, workspace=workspace)
     own_out, own_ws = out is None, workspace is None
     if own_out:
         out = torch.empty((B, hq, d), dtype=q.dtype, device=q.device)

@@ -1,5 +1,7 @@
-"""Build libpkv.so in-tree for gfx950 with hipcc (objects compiled in parallel,
-then linked). Usage: ``python -m paged_kv_cache_125_amd.build``."""
+"""Build libpkv.so (the attention library) and libpkv_probe.so (the streaming
+read reference the benchmark times beside it) in-tree for gfx950 with hipcc:
+objects compiled in parallel, then linked. Usage:
+``python -m paged_kv_cache_125_amd.build``."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -13,8 +15,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 
 SOURCES = ["api.hip", "store.hip", "rope.hip", "decode.hip", "prefill.hip", "pack.cpp", "block_manager.cpp"]
+PROBE_SOURCES = ["probe.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
@@ -38,18 +42,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -17,15 +17,16 @@
 //    a freed block later reused under another prefix chain keeps an entry
 //    under its old hash and may hold the same tokens, but its KV was computed
 //    in the other context, so that stale entry must miss too;
-//  - allocating a sequence walks its logical blocks: until the first miss,
-//    full blocks found in the table are shared (reference count + 1, or taken
-//    back from the free FIFO if nobody holds them) and count as cached tokens;
-//    from the first miss on, every block is fresh from the front of the FIFO.
-//    Every full block's hash and tokens are (re)registered;
-//  - before a decode step writes the KV of a sequence's newest token, the
-//    sequence gets a new block when that token opens one (len % bs == 1), and
-//    the last block is hashed and registered when that token fills it
-//    (len % bs == 0);
+//  - a new sequence's cached prefix is the longest run of its leading full
+//    blocks whose chained hash is registered to a block holding exactly those
+//    tokens. Those blocks are shared (one more holder each; a block nobody
+//    held comes back out of the free FIFO with its K/V intact) and count as
+//    cached tokens. Every later block is fresh from the front of the FIFO,
+//    and the fresh full ones are registered;
+//  - before a decode step writes the KV of a sequence's newest token (at
+//    position len - 1), the sequence gets a new block when that position
+//    lies past its table, and the block is hashed and registered when that
+//    position is the block's last;
 //  - deallocation drops one reference per block, last block first; blocks
 //    reaching zero return to the back of the FIFO but keep their hash and
 //    tokens, so a later allocation of the same prefix can still hit them.
@@ -34,6 +35,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -179,12 +181,28 @@ struct pkv_block_manager {
         x.hashed = false;
         x.tokens.clear();
     }
+    // A free block whose K/V a new holder reuses: it leaves the FIFO and keeps
+    // its registration.
+    void revive(int32_t b) {
+        unlink_free(b);
+        blocks[b].ref = 1;
+    }
     void record(int32_t b, uint64_t h, const int64_t *tok, int32_t n) {
         Block &x = blocks[b];
         x.hashed = true;
         x.hash = h;
         x.tokens.assign(tok, tok + n);
         by_hash[h] = b;
+    }
+    // The block registered under hash h, if it still holds exactly these
+    // tokens under that hash (a hash collision or a stale entry is a miss).
+    int32_t lookup(uint64_t h, const int64_t *tok, int32_t n) const {
+        auto it = by_hash.find(h);
+        if (it == by_hash.end()) return -1;
+        const Block &c = blocks[it->second];
+        const bool same = c.hashed && c.hash == h && c.tokens.size() == (size_t)n &&
+                          memcmp(c.tokens.data(), tok, (size_t)n * 8) == 0;
+        return same ? it->second : -1;
     }
     int32_t blocks_for(int64_t len) const { return (int32_t)((len + block_size - 1) / block_size); }
 };
@@ -224,46 +242,44 @@ extern "C" int pkv_bm_allocate(pkv_block_manager *m, int64_t seq_id, const int64
     if (!m || num_tokens < 1 || !token_ids)
         return pkv_internal_fail(PKV_EINVAL, "pkv_bm_allocate: bad arguments");
     if (m->seqs.count(seq_id)) return pkv_internal_fail(PKV_EINVAL, "pkv_bm_allocate: sequence already holds blocks");
-    const int32_t nb = m->blocks_for(num_tokens), bs = m->block_size;
+    const int32_t bs = m->block_size;
+    const int32_t nb = m->blocks_for(num_tokens);
+    const int32_t nfull = (int32_t)(num_tokens / bs);   // blocks the prompt fills completely
     // The worst case (no hit) must fit before anything changes.
     if (m->num_free < nb) return pkv_internal_fail(PKV_ENOSPACE, "pkv_bm_allocate: not enough free blocks");
+
+    // 1. The identity of every full block: its hash chained to the block before.
+    std::vector<uint64_t> ident((size_t)nfull);
+    for (int32_t i = 0; i < nfull; ++i)
+        ident[i] = block_hash(token_ids + (int64_t)i * bs, bs, i > 0, i > 0 ? ident[i - 1] : 0);
+
+    // 2. The cached prefix: the longest run of leading full blocks whose
+    //    identity is registered to a block holding exactly these tokens.
     SeqState st;
     st.tokens.assign(token_ids, token_ids + num_tokens);
     st.table.reserve(nb);
-    bool miss = false, have_prev = false;
-    uint64_t prev = 0;
-    for (int32_t i = 0; i < nb; ++i) {
-        const int64_t *tok = token_ids + (int64_t)i * bs;
-        const int32_t n = (int32_t)((int64_t)(i + 1) * bs <= num_tokens ? bs : num_tokens - (int64_t)i * bs);
-        const bool full = n == bs;
-        uint64_t h = 0;
-        int32_t hit = -1;
-        if (full) {
-            h = block_hash(tok, n, have_prev, prev);
-            auto it = m->by_hash.find(h);
-            if (it != m->by_hash.end()) {
-                const Block &c = m->blocks[it->second];
-                if (c.hashed && c.hash == h && c.tokens.size() == (size_t)n &&
-                    memcmp(c.tokens.data(), tok, (size_t)n * 8) == 0)
-                    hit = it->second;
-            }
-        }
-        if (hit < 0) miss = true;
-        int32_t b;
-        if (miss) {
-            b = m->free_head;
-            m->take(b);
-        } else {
-            b = hit;
-            st.num_cached += bs;
-            if (m->blocks[b].ref > 0) ++m->blocks[b].ref;
-            else m->take(b);
-        }
-        if (full) m->record(b, h, tok, n);
+    int32_t shared = 0;
+    for (; shared < nfull; ++shared) {
+        const int32_t b = m->lookup(ident[shared], token_ids + (int64_t)shared * bs, bs);
+        if (b < 0) break;
         st.table.push_back(b);
-        // the chain continues from this block's hash (a partial block ends it)
-        have_prev = full;
-        prev = h;
+    }
+
+    // 3. Claim the prefix: one more holder per block; a block nobody held
+    //    leaves the free FIFO (its K/V is still valid, so it is reused as is).
+    for (int32_t b : st.table) {
+        if (m->blocks[b].ref > 0) ++m->blocks[b].ref;
+        else m->revive(b);
+    }
+    st.num_cached = shared * bs;
+
+    // 4. The rest are fresh blocks from the front of the FIFO. The full ones
+    //    are registered, so that a later prompt with this prefix finds them.
+    for (int32_t i = shared; i < nb; ++i) {
+        const int32_t b = m->free_head;
+        m->take(b);
+        if (i < nfull) m->record(b, ident[i], token_ids + (int64_t)i * bs, bs);
+        st.table.push_back(b);
     }
     if (num_cached_tokens) *num_cached_tokens = st.num_cached;
     m->seqs.emplace(seq_id, std::move(st));
@@ -293,29 +309,35 @@ extern "C" int pkv_bm_may_append(pkv_block_manager *m, int64_t seq_id) {
     if (it == m->seqs.end()) return pkv_internal_fail(PKV_EINVAL, "pkv_bm_may_append: unknown sequence");
     SeqState &st = it->second;
     const int32_t bs = m->block_size;
-    const int64_t len = (int64_t)st.tokens.size();
-    if (st.table.empty()) return pkv_internal_fail(PKV_EINVAL, "pkv_bm_may_append: sequence has no blocks");
-    const int32_t need = m->blocks_for(len), have = (int32_t)st.table.size();
-    if (need == have + 1) {
-        // the newest token opens a block (len % bs == 1 for bs > 1): the
-        // previous block must be complete
+    if (st.table.empty() || st.tokens.empty())
+        return pkv_internal_fail(PKV_EINVAL, "pkv_bm_may_append: sequence has no blocks");
+    // Where the newest token's K/V goes: logical block lb, offset off in it.
+    const int64_t pos = (int64_t)st.tokens.size() - 1;
+    const int64_t lb = pos / bs;
+    const int32_t off = (int32_t)(pos % bs);
+    const int64_t have = (int64_t)st.table.size();
+    if (lb == have) {
+        // A block past the table: the one before must be complete, and a
+        // fresh block is needed for this token.
         if (!m->blocks[st.table.back()].hashed)
             return pkv_internal_fail(PKV_EINVAL, "pkv_bm_may_append: last block not complete");
         if (m->num_free < 1) return pkv_internal_fail(PKV_ENOSPACE, "pkv_bm_may_append: no free block");
         const int32_t b = m->free_head;
         m->take(b);
         st.table.push_back(b);
-    } else if (need != have) {
+    } else if (lb != have - 1) {
         return pkv_internal_fail(PKV_EINVAL, "pkv_bm_may_append: sequence length out of step with its blocks");
     }
-    Block &last = m->blocks[st.table.back()];
-    if (last.hashed) return pkv_internal_fail(PKV_EINVAL, "pkv_bm_may_append: last block already complete");
-    if (len % bs == 0) {
-        // the newest token fills the last block: register it, chained to the previous one
-        const bool hp = st.table.size() > 1;
-        const uint64_t prefix = hp ? m->blocks[st.table[st.table.size() - 2]].hash : 0;
-        const int64_t *tok = &st.tokens[len - bs];
-        m->record(st.table.back(), block_hash(tok, bs, hp, prefix), tok, bs);
+    const int32_t cur = st.table.back();
+    if (m->blocks[cur].hashed)
+        return pkv_internal_fail(PKV_EINVAL, "pkv_bm_may_append: last block already complete");
+    if (off == bs - 1) {
+        // This token completes its block: register it under its chained
+        // identity so that a later prompt sharing these tokens can reuse it.
+        const bool chained = lb > 0;
+        const uint64_t before = chained ? m->blocks[st.table[lb - 1]].hash : 0;
+        const int64_t *tok = st.tokens.data() + lb * bs;
+        m->record(cur, block_hash(tok, bs, chained, before), tok, bs);
     }
     return PKV_OK;
 }
@@ -324,11 +346,13 @@ extern "C" int pkv_bm_deallocate(pkv_block_manager *m, int64_t seq_id) {
     if (!m) return pkv_internal_fail(PKV_EINVAL, "pkv_bm_deallocate: null manager");
     auto it = m->seqs.find(seq_id);
     if (it == m->seqs.end()) return pkv_internal_fail(PKV_EINVAL, "pkv_bm_deallocate: unknown sequence");
+    // Released tail first: a sequence's leading blocks -- the ones other
+    // prompts are most likely to share -- reach the back of the FIFO last and
+    // are therefore the last to be handed out again (and lose their K/V).
     const std::vector<int32_t> &t = it->second.table;
-    for (size_t i = t.size(); i-- > 0;) {
-        Block &b = m->blocks[t[i]];
-        if (--b.ref == 0) m->push_back_free(t[i]);
-    }
+    std::for_each(t.rbegin(), t.rend(), [m](int32_t b) {
+        if (--m->blocks[b].ref == 0) m->push_back_free(b);
+    });
     m->seqs.erase(it);
     return PKV_OK;
 }

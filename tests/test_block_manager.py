@@ -130,6 +130,19 @@ def test_released_blocks_stay_hits_until_reused():
     assert m.num_free == 1
 
 
+def test_a_revived_block_stays_registered():
+    # blocks released by one sequence and taken back by a later prompt with
+    # the same prefix keep their registration: a third prompt with that prefix
+    # still finds them while the second holds them
+    m = pkv.BlockManager(6, 2)
+    m.allocate(1, [1, 2, 3, 4])
+    t = m.block_table(1)
+    m.deallocate(1)
+    assert m.allocate(2, [1, 2, 3, 4, 5]) == 4
+    assert m.allocate(3, [1, 2, 3, 4, 9]) == 4
+    assert m.block_table(3)[:2] == t == m.block_table(2)[:2]
+
+
 def test_a_stale_entry_with_the_same_tokens_is_a_miss():
     # block X holds tokens T after prefix P1, is freed, and is reused for T
     # after prefix P2; P1 + T must then miss although X's tokens equal T

@@ -17,7 +17,11 @@
    current stream's next allocation before the kernels have run.
 
 Only packs, uploads, spin kernels, decode calls on valid inputs and prefill
-calls whose out-of-range rows stay inside the same small tensors run here."""
+calls whose out-of-range rows lie inside memory the test itself allocated run
+here: q, k, v and out are allocated with rows to spare past the claimed range,
+filled with a sentinel, and the call is handed views of their first total_q
+rows. A regressed guard would then read and write those spare rows, which the
+test owns and checks, instead of memory past an allocation."""
 import numpy as np
 import pytest
 import torch
@@ -62,15 +66,18 @@ def test_staging_buffer_outlives_its_queued_upload(cuda):
 def test_prefill_skips_sequence_outside_total_q(cuda, dtype, paged):
     say(f"[gpu] prefill: a sequence whose cu_seqlens overrun total_q is skipped ({dtype}, paged={paged})")
     hq, hkv, d, bs = 8, 4, 128, 16
-    total, n0 = 200, 100
+    total, n0, spare = 200, 100, 256
     gen = torch.Generator().manual_seed(11)
-    q = torch.randn(total, hq, d, generator=gen).to(dtype)
-    k = torch.randn(total, hkv, d, generator=gen).to(dtype)
-    v = torch.randn(total, hkv, d, generator=gen).to(dtype)
-    # sequence 1 claims rows [100, 230) of a 200-row batch
+    q = torch.randn(spare, hq, d, generator=gen).to(dtype)
+    k = torch.randn(spare, hkv, d, generator=gen).to(dtype)
+    v = torch.randn(spare, hkv, d, generator=gen).to(dtype)
+    # sequence 1 claims rows [100, 230) of a 200-row batch; the tensors hold
+    # 256 rows, of which the call sees the first 200
     cu = torch.tensor([0, n0, n0 + 130], dtype=torch.int32, device="cuda")
     sentinel = 7.0
-    out = torch.full((total, hq, d), sentinel, dtype=dtype, device="cuda")
+    out_all = torch.full((spare, hq, d), sentinel, dtype=dtype, device="cuda")
+    out = out_all[:total]
+    qd, kd, vd = q.cuda()[:total], k.cuda()[:total], v.cuda()[:total]
     scale = d ** -0.5
     if paged:
         nb = 2 * (-(-230 // bs)) + 2
@@ -82,17 +89,18 @@ def test_prefill_skips_sequence_outside_total_q(cuda, dtype, paged):
         tables = torch.full((2, w), -1, dtype=torch.int32)
         tables[0, :-(-n0 // bs)] = torch.arange(-(-n0 // bs), dtype=torch.int32)
         tables[1] = torch.arange(w, 2 * w, dtype=torch.int32)
-        pkv.prefill_attention_varlen(q.cuda(), cu, cu, 130, 130, scale, k_cache=kc.cuda(),
+        pkv.prefill_attention_varlen(qd, cu, cu, 130, 130, scale, k_cache=kc.cuda(),
                                      v_cache=vc.cuda(), block_tables=tables.cuda(), out=out)
     else:
-        pkv.prefill_attention_varlen(q.cuda(), cu, cu, 130, 130, scale, k=k.cuda(), v=v.cuda(), out=out)
+        pkv.prefill_attention_varlen(qd, cu, cu, 130, 130, scale, k=kd, v=vd, out=out)
     torch.cuda.synchronize()
     want = oracle.attention(q[:n0], [n0], [n0], hkv, scale, k=k[:n0], v=v[:n0])
     err = max_abs_err(out[:n0], want)
     bar = 2e-2 if dtype == torch.bfloat16 else 1e-4
     say(f"  sequence 0: max |err| = {err:.3e}")
     assert err <= bar
-    assert bool((out[n0:].float() == sentinel).all()), "rows of the skipped sequence were written"
+    # rows [100, 200) belong to the skipped sequence; [200, 256) lie past total_q
+    assert bool((out_all[n0:].float() == sentinel).all()), "rows of the skipped sequence were written"
 
 
 def test_binding_allocations_survive_work_on_another_stream(cuda):
