@@ -21,8 +21,9 @@
  *
  * Conventions for every device entry point:
  *  - All device pointers are caller-owned and must stay valid until the stream
- *    reaches the call. The library keeps no device state between calls, never
- *    synchronises, and allocates no device memory.
+ *    reaches the call. The library never synchronises and allocates no device
+ *    memory; the only device memory it owns is the fixed scratch array of
+ *    pkv_decode_attention_paged_noalloc, the only state kept between calls.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *  - Tensors are row-major; strides are in ELEMENTS. The caches are the
  *    per-layer views [num_blocks, block_size, num_kv_heads, head_dim],
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef enum {
     PKV_OK = 0,
@@ -196,6 +197,37 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t max_context_len,
                                   int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t block_size, int32_t dtype,
                                   int32_t partition_size);
+
+/* ---------------------------------------------------------------------------
+ * decode_attention_paged without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * that allocate nothing per step, harnesses that forbid hipMalloc. The
+ * computation, arguments and errors are those of pkv_decode_attention_paged;
+ * the workspace is instead a scratch array of PKV_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that the library holds on every device it runs on until the
+ * process ends. The call allocates nothing itself (the caller still provides
+ * q, the caches, the metadata and out).
+ *  - PKV_ENOSPACE when pkv_decode_workspace_bytes(...) for these arguments
+ *    exceeds PKV_NOALLOC_SCRATCH_BYTES (the balanced split needs about
+ *    waves * 2 * group * (head_dim + 2) * 4 bytes: 4.3 MB at 1024 waves,
+ *    group 4, head_dim 128; long fixed partitions can need more).
+ *  - The scratch of a device is found once, on the first call made with that
+ *    device current; `stream` must belong to the current device.
+ *  - Every call on a device shares that device's scratch and leaves its
+ *    contents behind (nothing in it needs to start zeroed). Calls that may
+ *    run at the same time on one device -- on different streams, or from
+ *    different host threads -- race on it; order them on one stream.
+ * -------------------------------------------------------------------------*/
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int pkv_decode_attention_paged_noalloc(const void *q, int64_t q_token_stride, const void *k_cache,
+                                       const void *v_cache, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                       int32_t num_seqs, int32_t max_context_len,
+                                       int32_t num_blocks, int32_t block_size,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, float scale, int32_t dtype, void *out,
+                                       int32_t partition_size, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Rotary embedding fused with store_kvcache (the step just before the KV write

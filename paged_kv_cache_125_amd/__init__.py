@@ -8,8 +8,8 @@ module raises on use -- there is no fallback path.
 
 Entry points (same names as the C functions, without the ``pkv_`` prefix):
 ``store_kvcache``, ``prefill_attention_varlen``, ``decode_attention_paged``,
-``decode_workspace_bytes``, ``decode_partition_size``, ``pack_prefill``,
-``pack_decode``.
+``decode_attention_paged_noalloc``, ``decode_workspace_bytes``,
+``decode_partition_size``, ``pack_prefill``, ``pack_decode``.
 """
 from __future__ import annotations
 
@@ -22,7 +22,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpkv.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 PKV_F32, PKV_BF16 = 0, 1
 _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_ELAUNCH", 4: "PKV_ENOSPACE"}
@@ -30,6 +30,7 @@ _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_ELAUNCH"
 EXPORTED = [
     "pkv_abi_version", "pkv_last_error", "pkv_store_kvcache", "pkv_prefill_attention_varlen",
     "pkv_decode_attention_paged", "pkv_decode_partition_size", "pkv_decode_workspace_bytes",
+    "pkv_decode_attention_paged_noalloc",
     "pkv_plan_prefill", "pkv_pack_prefill", "pkv_plan_decode", "pkv_pack_decode", "pkv_upload",
     "pkv_rope_cos_sin_table", "pkv_rope_store_kvcache",
     "pkv_xxh64", "pkv_block_hash", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
@@ -80,6 +81,9 @@ def lib():
     L.pkv_decode_attention_paged.restype = ctypes.c_int
     L.pkv_decode_attention_paged.argtypes = [P, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
                                              i32, f32, i32, P, i32, P, sz, P]
+    L.pkv_decode_attention_paged_noalloc.restype = ctypes.c_int
+    L.pkv_decode_attention_paged_noalloc.argtypes = [P, i64, P, P, P, i32, P, i32, i32, i32, i32, i32,
+                                                     i32, i32, f32, i32, P, i32, P]
     L.pkv_decode_partition_size.restype = i32
     L.pkv_decode_partition_size.argtypes = [i32] * 8
     L.pkv_decode_workspace_bytes.restype = sz
@@ -490,6 +494,36 @@ def decode_attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         float(scale), _dtype_code(q), _ptr(out), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream)))
     _used_on(stream, out if own_out else None, workspace if own_ws else None)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attention_paged_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                   max_context_len: int, scale: float, out: torch.Tensor, *,
+                                   partition_size: int = 0, stream=None) -> torch.Tensor:
+    """pkv_decode_attention_paged_noalloc: decode_attention_paged with the
+    library's own device scratch as workspace, for callers that cannot
+    allocate. ``out`` must be given; nothing is allocated on the path. Calls
+    that may overlap on one GPU race on its scratch."""
+    _need(q.dim() == 3, "q must be [num_seqs, num_q_heads, head_dim]")
+    _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
+    B, hq, d = q.shape
+    _rows(q, "q", hq, d, q.dtype, 0)
+    _pool(k_cache, v_cache, q.dtype)
+    nb, bs, hkv, _ = k_cache.shape
+    _need(k_cache.shape[3] == d, "cache head_dim differs from q's")
+    _int32_table(block_tables, "block_tables", B)
+    _int32_vec(context_lens, "context_lens", B)
+    _out(out, q)
+    _one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+             context_lens=context_lens, out=out)
+    _check(lib().pkv_decode_attention_paged_noalloc(
+        _ptr(q), _token_stride(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), B, int(max_context_len), nb, bs, hq, hkv, d,
+        float(scale), _dtype_code(q), _ptr(out), int(partition_size), _stream(stream)))
     return out
 
 

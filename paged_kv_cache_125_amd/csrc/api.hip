@@ -1,8 +1,11 @@
 // api.hip -- the extern "C" entry points of libpkv (declared in include/pkv.h):
 // host-side validation, launch configuration and workspace layout. No device
-// memory is allocated and nothing synchronises.
+// memory is allocated and nothing synchronises; the one library-owned device
+// buffer is the static decode scratch below.
 #include <stdarg.h>
 #include <stdio.h>
+
+#include <mutex>
 
 #include <math.h>
 
@@ -276,13 +279,50 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t max_conte
                                     block_size, dtype, partition_size).total;
 }
 
-extern "C" int pkv_decode_attention_paged(
-    const void *q, int64_t q_token_stride, const void *k_cache, const void *v_cache,
-    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
-    int32_t num_seqs, int32_t max_context_len, int32_t num_blocks, int32_t block_size,
-    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t dtype,
-    void *out, int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream) {
-    const char *fn = "pkv_decode_attention_paged";
+// ---------------------------------------------------------------------------
+// Library-owned scratch for pkv_decode_attention_paged_noalloc: the decode
+// workspace (partial results and the split's prefix sums) for callers that
+// cannot allocate device memory. Each device holds one copy of this array for
+// the life of the process. In host code `scratch` only names the array for the
+// runtime; its address on a device comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and only that address reaches a
+// kernel.
+constexpr size_t kNoAllocScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];   // device address of `scratch`, per device
+
+// The current device's copy of `scratch`.
+int scratch_address(const char *fn, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PKV_ELAUNCH, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(PKV_EUNSUPPORTED, "%s: device %d", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PKV_ELAUNCH, "%s: hipGetSymbolAddress: %s", fn, hipGetErrorString(e));
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return PKV_OK;
+}
+
+// Shared body of the two decode entry points. With use_scratch the workspace
+// is the current device's `scratch` (the plan must fit in it), otherwise the
+// caller's.
+int decode_call(const char *fn, const void *q, int64_t q_token_stride, const void *k_cache,
+                const void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                int32_t num_blocks, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                int32_t head_dim, float scale, int32_t dtype, void *out, int32_t partition_size,
+                void *workspace, size_t workspace_bytes, bool use_scratch, void *stream) {
     int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs, scale);
     if (rc) return rc;
     if (max_context_len < 0) return fail(PKV_EINVAL, "%s: negative max_context_len", fn);
@@ -299,6 +339,17 @@ extern "C" int pkv_decode_attention_paged(
         return fail(PKV_EINVAL, "%s: q/out must be 16-byte aligned with 16-byte strides", fn);
     const pkv::DecodePlan ws = pkv::plan_decode(num_seqs, max_context_len, num_q_heads, num_kv_heads,
                                                 head_dim, block_size, dtype, partition_size);
+    if (use_scratch) {
+        if (ws.total > (int64_t)kNoAllocScratchBytes)
+            return fail(PKV_ENOSPACE, "%s: needs %lld bytes of scratch, more than the library's %zu",
+                        fn, (long long)ws.total, kNoAllocScratchBytes);
+        workspace = nullptr;
+        workspace_bytes = kNoAllocScratchBytes;
+        if (ws.total > 0) {
+            rc = scratch_address(fn, &workspace);
+            if (rc) return rc;
+        }
+    }
     if ((int64_t)workspace_bytes < ws.total)
         return fail(PKV_ENOSPACE, "%s: workspace needs %lld bytes", fn, (long long)ws.total);
     if (ws.total > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
@@ -329,6 +380,32 @@ extern "C" int pkv_decode_attention_paged(
     a.ws_ml = ws.total ? (float *)((char *)workspace + ws.acc_bytes) : nullptr;
     a.ws_cum = ws.cum_bytes ? (int32_t *)((char *)workspace + ws.acc_bytes + ws.ml_bytes) : nullptr;
     return launched(pkv::launch_decode(a, ws, dtype, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+extern "C" int pkv_decode_attention_paged(
+    const void *q, int64_t q_token_stride, const void *k_cache, const void *v_cache,
+    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+    int32_t num_seqs, int32_t max_context_len, int32_t num_blocks, int32_t block_size,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t dtype,
+    void *out, int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_call("pkv_decode_attention_paged", q, q_token_stride, k_cache, v_cache,
+                       block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+                       num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                       out, partition_size, workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int pkv_decode_attention_paged_noalloc(
+    const void *q, int64_t q_token_stride, const void *k_cache, const void *v_cache,
+    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+    int32_t num_seqs, int32_t max_context_len, int32_t num_blocks, int32_t block_size,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, int32_t dtype,
+    void *out, int32_t partition_size, void *stream) {
+    return decode_call("pkv_decode_attention_paged_noalloc", q, q_token_stride, k_cache, v_cache,
+                       block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+                       num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                       out, partition_size, nullptr, 0, true, stream);
 }
 
 extern "C" int pkv_upload(const void *host_buf, void *dev_buf, size_t bytes, void *stream) {
