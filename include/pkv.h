@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 typedef enum {
     PKV_OK = 0,
@@ -129,9 +129,28 @@ int pkv_store_kvcache(const void *k, const void *v, int64_t k_token_stride,
  *                  unwritten).
  *  max_seqlen_q/_k host upper bounds of Lq_s / Lk_s (size the launch grid).
  *  dtype           PKV_BF16 (MFMA path for head_dim 128) or PKV_F32.
+ *  workspace       NULL (with workspace_bytes 0): one workgroup per
+ *                  (sequence, kv head, query block) item, laid out longest
+ *                  first so that the hardware's own dispatch balances the
+ *                  batch. Non-NULL: device memory of
+ *                  pkv_prefill_workspace_bytes() bytes, 256-byte aligned,
+ *                  ZEROED ONCE when it is allocated, holding the counters of
+ *                  the persistent grid: two workgroups per CU whatever the
+ *                  batch, which claim items as they go. Each call leaves it
+ *                  zeroed again when it completes, so it is reused call after
+ *                  call without clearing; calls that may run at the same time
+ *                  (on different streams) need workspaces of their own.
+ *                  Batches beyond the persistent grid's tables (more than
+ *                  2048 (sequence, kv head) pairs or 512 query blocks) take
+ *                  one workgroup per item and leave the workspace untouched.
+ *                  Both grids give bit-identical results; on the batches
+ *                  measured so far the one-workgroup-per-item grid is the
+ *                  faster one. Only the bf16 head_dim-128 kernel has the
+ *                  persistent grid; the others ignore the workspace.
  * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128}, a
  * positive finite scale, and block_size a power of two in [1, 1024] when
- * block_tables != NULL. */
+ * block_tables != NULL. PKV_ENOSPACE if a non-NULL workspace is smaller than
+ * pkv_prefill_workspace_bytes(). */
 int pkv_prefill_attention_varlen(const void *q, int64_t q_token_stride, const void *k,
                                  const void *v, int64_t kv_token_stride, const void *k_cache,
                                  const void *v_cache, const int32_t *block_tables,
@@ -140,7 +159,13 @@ int pkv_prefill_attention_varlen(const void *q, int64_t q_token_stride, const vo
                                  int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                  int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, float scale,
-                                 int32_t dtype, void *out, void *stream);
+                                 int32_t dtype, void *out, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* Workspace bytes pkv_prefill_attention_varlen needs (a constant 256: the
+ * persistent grid's counters; the arguments are those of the call). */
+size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
 
 /* ---------------------------------------------------------------------------
  * decode_attention_paged  ([MR] "prepare_decode": one query per sequence,

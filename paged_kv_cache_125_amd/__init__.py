@@ -22,7 +22,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpkv.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 PKV_F32, PKV_BF16 = 0, 1
 _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_ELAUNCH", 4: "PKV_ENOSPACE"}
@@ -30,7 +30,7 @@ _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_ELAUNCH"
 EXPORTED = [
     "pkv_abi_version", "pkv_last_error", "pkv_store_kvcache", "pkv_prefill_attention_varlen",
     "pkv_decode_attention_paged", "pkv_decode_partition_size", "pkv_decode_workspace_bytes",
-    "pkv_decode_attention_paged_noalloc",
+    "pkv_decode_attention_paged_noalloc", "pkv_prefill_workspace_bytes",
     "pkv_plan_prefill", "pkv_pack_prefill", "pkv_plan_decode", "pkv_pack_decode", "pkv_upload",
     "pkv_rope_cos_sin_table", "pkv_rope_store_kvcache",
     "pkv_xxh64", "pkv_block_hash", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
@@ -77,7 +77,9 @@ def lib():
     L.pkv_store_kvcache.argtypes = [P, P, i64, i64, P, P, P, i32, i32, i32, i32, i32, i32, P]
     L.pkv_prefill_attention_varlen.restype = ctypes.c_int
     L.pkv_prefill_attention_varlen.argtypes = [P, i64, P, P, i64, P, P, P, i32, P, P, i32, i32, i32,
-                                               i32, i32, i32, i32, i32, i32, f32, i32, P, P]
+                                               i32, i32, i32, i32, i32, i32, f32, i32, P, P, sz, P]
+    L.pkv_prefill_workspace_bytes.restype = sz
+    L.pkv_prefill_workspace_bytes.argtypes = [i32] * 6
     L.pkv_decode_attention_paged.restype = ctypes.c_int
     L.pkv_decode_attention_paged.argtypes = [P, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
                                              i32, f32, i32, P, i32, P, sz, P]
@@ -384,6 +386,12 @@ def rope_store_kvcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cach
         hq, hkv, d, _dtype_code(q), _stream(stream)))
 
 
+def prefill_workspace_bytes() -> int:
+    """pkv_prefill_workspace_bytes: the size of the workspace that selects the
+    persistent prefill grid."""
+    return int(lib().pkv_prefill_workspace_bytes(0, 0, 0, 0, 0, 0))
+
+
 def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
                              max_seqlen_q: int, max_seqlen_k: int, scale: float, *,
                              k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
@@ -391,9 +399,14 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
                              v_cache: Optional[torch.Tensor] = None,
                              block_tables: Optional[torch.Tensor] = None,
                              num_kv_heads: Optional[int] = None,
-                             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                             out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
     """pkv_prefill_attention_varlen. Keys from k/v, or from the caches through
-    block_tables when given."""
+    block_tables when given. Without ``workspace`` one workgroup runs per
+    item; a ``workspace`` (uint8, >= prefill_workspace_bytes(), zeroed once
+    when allocated and left zeroed by every call) selects the persistent grid
+    and must not be shared by calls that may overlap."""
     _need(q.dim() == 3, "q must be [tokens, num_q_heads, head_dim]")
     _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
     total_q, hq, d = q.shape
@@ -428,14 +441,19 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
     _one_gpu(q=q, k=k, v=v, k_cache=k_cache if block_tables is not None else None,
              v_cache=v_cache if block_tables is not None else None, block_tables=block_tables,
              cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, out=out)
+    if workspace is not None:
+        _need(workspace.dtype == torch.uint8 and workspace.is_contiguous()
+              and workspace.device == q.device, "workspace must be a contiguous uint8 tensor on q's device")
     own_out = out is None
     if own_out:
         out = torch.empty((total_q, hq, d), dtype=q.dtype, device=q.device)
+    _need(workspace is None or workspace.numel() >= prefill_workspace_bytes(),
+          "workspace is smaller than prefill_workspace_bytes()")
     _check(lib().pkv_prefill_attention_varlen(
         _ptr(q), _token_stride(q), _ptr(k), _ptr(v), kv_stride, _ptr(k_cache), _ptr(v_cache),
         _ptr(block_tables), maxb, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, total_q,
         int(max_seqlen_q), int(max_seqlen_k), nb, bs, hq, hkv, d, float(scale), _dtype_code(q),
-        _ptr(out), _stream(stream)))
+        _ptr(out), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
     if own_out:
         _used_on(stream, out)
     return out

@@ -198,7 +198,8 @@ extern "C" int pkv_prefill_attention_varlen(
     int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
     int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
     int32_t num_blocks, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, float scale, int32_t dtype, void *out, void *stream) {
+    int32_t head_dim, float scale, int32_t dtype, void *out, void *workspace,
+    size_t workspace_bytes, void *stream) {
     const char *fn = "pkv_prefill_attention_varlen";
     int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs, scale);
     if (rc) return rc;
@@ -213,7 +214,15 @@ extern "C" int pkv_prefill_attention_varlen(
         return fail(PKV_EINVAL, "%s: q token stride smaller than a row", fn);
     if (!aligned16(q) || !aligned16(out) || (q_token_stride * es) % 16)
         return fail(PKV_EINVAL, "%s: q/out must be 16-byte aligned with 16-byte strides", fn);
+    if (workspace) {
+        if (workspace_bytes < pkv::kPrefillWorkspaceBytes)
+            return fail(PKV_ENOSPACE, "%s: workspace needs %zu bytes", fn, pkv::kPrefillWorkspaceBytes);
+        if ((uintptr_t)workspace & 255u) return fail(PKV_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+    } else if (workspace_bytes) {
+        return fail(PKV_EINVAL, "%s: null workspace with a nonzero size", fn);
+    }
     pkv::PrefillArgs a;
+    a.work_ctr = (uint32_t *)workspace;
     a.q = q;
     a.q_stride = q_token_stride;
     a.paged = block_tables != nullptr;
@@ -259,6 +268,10 @@ extern "C" int pkv_prefill_attention_varlen(
         a.by_rank = keys * num_kv_heads * head_dim * 2 * 2 <= (int64_t(128) << 20);
     }
     return launched(pkv::launch_prefill(a, dtype, (hipStream_t)stream), fn);
+}
+
+extern "C" size_t pkv_prefill_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) {
+    return pkv::kPrefillWorkspaceBytes;
 }
 
 extern "C" int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t max_context_len,

@@ -88,7 +88,10 @@ struct PrefillArgs {
     int32_t max_seqlen_k;      // a sequence with more keys (or fewer than its queries) is skipped
     int32_t total_q;           // rows of q and out; a sequence outside them is skipped
     int32_t by_rank;           // grid order: longest query blocks first across pairs (set by the host)
+    uint32_t *work_ctr;        // persistent grid: 8 per-XCD claim counters + 1 exit counter, or null
 };
+// Bytes of the prefill workspace (the persistent grid's counters).
+constexpr size_t kPrefillWorkspaceBytes = 256;
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream);
 
 }  // namespace pkv

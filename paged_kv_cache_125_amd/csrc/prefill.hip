@@ -26,6 +26,8 @@
 // produced. V stays row-major in LDS; the V^T operand comes from the gfx950
 // transpose read (ds_read_b64_tr_b16), two reads of 4 consecutive keys per
 // MFMA. A wave skips key tiles that lie entirely above its causal diagonal.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -36,6 +38,10 @@ namespace pkv {
 constexpr int kPfD = 128;
 constexpr int kPfBN = 64;      // keys per tile
 constexpr float kLazy = 8.f;   // log2 headroom before the running max is moved
+// Persistent prefill grid: the largest per-XCD pair count and query-block
+// count whose item tables fit in LDS (larger batches take the fixed grid).
+constexpr int kPfMaxXcdPairs = 256;
+constexpr int kPfMaxQblocks = 512;
 
 // Element offset of key `key` of sequence s in its source (k rows or the
 // pool), for kv head kvh; -1 when the table entry is outside the pool.
@@ -66,10 +72,14 @@ __device__ __forceinline__ int tile_swz(int t) { return ((t & 3) << 2) | ((t >> 
 
 // NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
 // owns BM = 32 * RB * NW rows of one query head. WPE waves share one SIMD.
-template <int SRC, int NW, int RB, int WPE>
+template <int SRC, int NW, int RB, int WPE, int HPW, bool PERSIST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_mfma_kernel(PrefillArgs a) {
-    constexpr int BM = 32 * RB * NW;
+    // HPW query heads of one kv head share the workgroup (and every K/V tile
+    // it stages); each head gets NW / HPW waves of RB blocks of 32 rows.
+    constexpr int WPH = NW / HPW;            // waves per head
+    constexpr int BM = 32 * RB * WPH;        // query rows per workgroup
+    static_assert(NW % HPW == 0, "heads must split the waves evenly");
     constexpr int LPW = 16 / NW;   // 1 KiB direct-load instructions per wave per K (or V) tile
     static_assert(NW * LPW == 16 && NW >= 2, "waves must split a tile evenly");
     static_assert(RB == 1 || RB == 2, "row blocks per wave");
@@ -95,28 +105,23 @@ void prefill_mfma_kernel(PrefillArgs a) {
     //    pairs' K/V are live at a time.
     // Either way the group's heads sit side by side and every (pair, query
     // block, head) is visited once.
+    const int HG = a.group / HPW;            // head groups per kv head
     const int qblocks = (a.max_seqlen_q + BM - 1) / BM;
-    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    int lp, rank, head;
-    if (a.by_rank) {
-        const int per_rank = ((a.num_seqs * a.Hkv + 7) / 8) * a.group;
-        rank = local / per_rank;
-        const int within = local - rank * per_rank;
-        lp = within / a.group;
-        head = within - lp * a.group;
-    } else {
-        const int per_pair = qblocks * a.group;
-        lp = local / per_pair;
-        const int within = local - lp * per_pair;
-        rank = within / a.group;
-        head = within - rank * a.group;
-    }
-    const int pair = 8 * lp + xcd;
-    if (pair >= a.num_seqs * a.Hkv) return;
+    const int npairs = a.num_seqs * a.Hkv;
+    const int xcd = blockIdx.x & 7;
+    const int hh = wave / WPH, wh = wave - hh * WPH;   // the wave's head in the group, its place in the head
+
+    // Persistent grid: the claim of the next item, issued by thread 0 once an
+    // item's tile loop is done (so that the per-tile waits for vector memory
+    // do not wait for it) and published after the item.
+    uint32_t next_claim = 0;
+    uint32_t *const claim_ctr = PERSIST ? a.work_ctr + xcd : nullptr;
+
+    // One work item: query block qt of (sequence, kv head) pair `pair`, head group hg.
+    auto run_item = [&](const int pair, const int qt, const int hg) {
     const int s = pair / a.Hkv;
     const int kvh = pair - s * a.Hkv;
-    const int qt = qblocks - 1 - rank;
-    const int h = kvh * a.group + head;
+    const int h = kvh * a.group + hg * HPW + hh;
     // All four bounds in one round trip (a workgroup with no rows here
     // learns it from the first two and leaves).
     const int q_start = a.cu_q[s], q_end = a.cu_q[s + 1];
@@ -134,13 +139,13 @@ void prefill_mfma_kernel(PrefillArgs a) {
     if (skip) return;
     const int off = Lk - Lq;
     const int r32 = lane & 31, j = lane >> 5;
-    // The wave owns rows q0 + 32*RB*wave + 32*rb + r32, rb < RB.
+    // The wave owns rows q0 + 32*RB*wh + 32*rb + r32, rb < RB.
     int my_pos[2];
     bool row_ok[2];
     bf16x8 qb[2][8];   // B operand of S^T = K Q^T: Q[row][d = 16*kk + 8*j .. +8]
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int row = q0 + 32 * RB * wave + 32 * rb + r32;
+        const int row = q0 + 32 * RB * wh + 32 * rb + r32;
         row_ok[rb] = row < Lq;
         my_pos[rb] = off + row;
         const uint16_t *q = (const uint16_t *)a.q + (int64_t)(q_start + row) * a.q_stride +
@@ -158,8 +163,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // keys for this wave, which skips their arithmetic (not their loads). A
     // wave whose rows all lie past the sequence's end (the last query block of
     // a sequence, or a short one such as a decode row) skips all of it.
-    const int pos_last = off + q0 + 32 * RB * (wave + 1) - 1;
-    const bool wave_rows = q0 + 32 * RB * wave < Lq;
+    const int pos_last = off + q0 + 32 * RB * (wh + 1) - 1;
+    const bool wave_rows = q0 + 32 * RB * wh < Lq;
 
     // Tile loads go global -> LDS directly (buffer_load_dwordx4 ... lds), no
     // registers in between. Instruction i of wave w fills LDS bytes
@@ -312,13 +317,17 @@ void prefill_mfma_kernel(PrefillArgs a) {
                         for (int r = 0; r < 16; ++r)
                             st[rb][mt][r] = (32 * mt + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : st[rb][mt][r];
                 }
-                float x = -INFINITY;
+                // four independent partial maxima, then a short tree
+                float xq[4];
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2)
-                        x = fmaxf(fmaxf(x, st[rb][mt][r]), st[rb][mt][r + 1]);
-                mx[rb] = xor32_max(x);
+                for (int g = 0; g < 4; ++g) {
+                    const int mt = g >> 1, r0 = 8 * (g & 1);
+                    xq[g] = fmaxf(fmaxf(st[rb][mt][r0], st[rb][mt][r0 + 1]), st[rb][mt][r0 + 2]);
+                    xq[g] = fmaxf(fmaxf(xq[g], st[rb][mt][r0 + 3]), st[rb][mt][r0 + 4]);
+                    xq[g] = fmaxf(fmaxf(xq[g], st[rb][mt][r0 + 5]), st[rb][mt][r0 + 6]);
+                    xq[g] = fmaxf(xq[g], st[rb][mt][r0 + 7]);
+                }
+                mx[rb] = xor32_max(fmaxf(fmaxf(xq[0], xq[1]), fmaxf(xq[2], xq[3])));
             }
             bool grow = false;
 #pragma unroll
@@ -342,6 +351,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const float mc = m[rb] * c;
+                float ls[4] = {0.f, 0.f, 0.f, 0.f};   // four short sum chains
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -351,9 +361,10 @@ void prefill_mfma_kernel(PrefillArgs a) {
                             pb[rb][mt][ap][e] = (__bf16)fast_exp2(__builtin_fmaf(st[rb][mt][8 * ap + e], c, -mc));
 #pragma unroll
                         for (int e = 0; e < 8; e += 2)
-                            l[rb] = __builtin_amdgcn_fdot2_f32_bf16(
-                                bf16x2{pb[rb][mt][ap][e], pb[rb][mt][ap][e + 1]}, ones, l[rb], false);
+                            ls[2 * mt + ap] = __builtin_amdgcn_fdot2_f32_bf16(
+                                bf16x2{pb[rb][mt][ap][e], pb[rb][mt][ap][e + 1]}, ones, ls[2 * mt + ap], false);
                     }
+                l[rb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
             }
             // O^T += V^T P^T over 4 steps of 16 keys; each V^T operand (two
             // transpose reads of 4 consecutive key rows) feeds both row blocks.
@@ -400,6 +411,10 @@ void prefill_mfma_kernel(PrefillArgs a) {
         __syncthreads();
     }
 
+    if constexpr (PERSIST) {
+        if (tid == 0)
+            next_claim = __hip_atomic_fetch_add(claim_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if constexpr (RB == 1) {
         // Through LDS (the tile buffers are free after the last barrier): the
         // wave's 32 x 128 output tile goes in with 8-byte writes, rows 272
@@ -419,7 +434,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 w[1] = pack_bf16x2(o[0][nt][4 * g + 2] * inv, o[0][nt][4 * g + 3] * inv);
                 *reinterpret_cast<u32x2 *>(stg + r32 * kPitch + 2 * (32 * nt + 8 * g + 4 * j)) = w;
             }
-        const int rbase = q0 + 32 * wave;
+        const int rbase = q0 + 32 * wh;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int rr = 4 * i + (lane >> 4), chunk = lane & 15;
@@ -435,7 +450,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
         const float lt = xor32_sum(l[rb]);
         if (!row_ok[rb]) continue;
         const float inv = 1.f / lt;
-        const int row = q0 + 32 * RB * wave + 32 * rb + r32;
+        const int row = q0 + 32 * RB * wh + 32 * rb + r32;
         uint16_t *out = (uint16_t *)a.out + ((int64_t)(q_start + row) * a.Hq + h) * kPfD;
         // o[rb][nt][4*g + c] = O[row][d = 32*nt + 8*g + 4*j + c]
 #pragma unroll
@@ -448,6 +463,152 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 *reinterpret_cast<u32x2 *>(out + 32 * nt + 8 * g + 4 * j) = w;
             }
     }
+    }
+    };
+
+    if constexpr (!PERSIST) {
+        // One workgroup per item, in a fixed XCD-aware order. The hardware
+        // hands workgroup p to XCD p % 8, and each XCD has its own L2. Work is
+        // grouped by (sequence, kv head) pair, the unit that shares K and V;
+        // pair pi runs on XCD pi % 8, so all query blocks and heads of that kv
+        // head read their K/V tiles through one L2. Two orders within an XCD,
+        // chosen on the host from the batch's K/V bytes (a bound on them when
+        // the keys come through block tables):
+        //  - K/V within half the 256 MB MALL: longest first across all the
+        //    XCD's pairs (query-block rank major), so the tail holds only
+        //    short blocks;
+        //  - larger: pair by pair, each pair's longest blocks first, so only a
+        //    few pairs' K/V are live at a time.
+        const int local = blockIdx.x >> 3;
+        int lp, rank, hg;
+        if (a.by_rank) {
+            const int per_rank = ((npairs + 7) / 8) * HG;
+            rank = local / per_rank;
+            const int within = local - rank * per_rank;
+            lp = within / HG;
+            hg = within - lp * HG;
+        } else {
+            const int per_pair = qblocks * HG;
+            lp = local / per_pair;
+            const int within = local - lp * per_pair;
+            rank = within / HG;
+            hg = within - rank * HG;
+        }
+        const int pair = 8 * lp + xcd;
+        if (pair >= npairs) return;
+        run_item(pair, qblocks - 1 - rank, hg);
+    } else {
+        // Persistent grid: a fixed number of workgroups per XCD, each claiming
+        // items of its XCD's list from a counter in the workspace (an
+        // agent-scope atomic). The list holds only the non-empty items of the
+        // XCD's pairs (pair = 8 * lp + xcd), in the same two orders as above,
+        // with pairs of more query blocks first; every workgroup builds it in
+        // LDS from cu_seqlens_q. An item's successor is claimed when its tile
+        // loop is done. A workgroup leaves when its claim passes the end of
+        // the list; the last one to leave zeroes the counters for the next call.
+        __shared__ int32_t s_nq[kPfMaxXcdPairs];      // query blocks per pair, sorted descending
+        __shared__ int32_t s_lp[kPfMaxXcdPairs];      // the pair (lp) at each sorted position
+        __shared__ int32_t s_raw[kPfMaxXcdPairs];     // query blocks per pair, by lp
+        __shared__ int32_t s_pre[kPfMaxQblocks + 1];  // items before rank r (or before sorted pair i)
+        __shared__ uint32_t s_claim;
+        uint32_t *ctr = a.work_ctr;
+        const int npx = (npairs + 7 - xcd) / 8;       // pairs of this XCD: lp < npx
+        for (int lp = tid; lp < npx; lp += 64 * NW) {
+            const int pair = 8 * lp + xcd;
+            const int sq = pair / a.Hkv;
+            const int lq = a.cu_q[sq + 1] - a.cu_q[sq];
+            s_raw[lp] = lq > 0 ? min((lq + BM - 1) / BM, qblocks) : 0;
+        }
+        if (tid == 0) s_claim = __hip_atomic_fetch_add(ctr + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        // stable sort by query-block count, descending (rank by counting)
+        for (int lp = tid; lp < npx; lp += 64 * NW) {
+            const int v = s_raw[lp];
+            int pos = 0;
+            for (int o = 0; o < npx; ++o) {
+                const int w = s_raw[o];
+                pos += (w > v) | ((w == v) & (o < lp));
+            }
+            s_nq[pos] = v;
+            s_lp[pos] = lp;
+        }
+        __syncthreads();
+        // prefix counts: rank-major over ranks r (query block qblocks-1-r; the
+        // pairs holding it are the first cnt of the sorted list), or
+        // pair-major over sorted pairs
+        const int nent = a.by_rank ? qblocks : npx;
+        if (tid < 64) {
+            int run = 0;
+            for (int base = 0; base < nent; base += 64) {
+                const int e = base + lane;
+                int cnt = 0;
+                if (e < nent) {
+                    if (a.by_rank) {
+                        const int qt = qblocks - 1 - e;   // pairs with s_nq > qt: binary search
+                        int lo = 0, hi = npx;
+                        while (lo < hi) {
+                            const int mid = (lo + hi) >> 1;
+                            if (s_nq[mid] > qt) lo = mid + 1; else hi = mid;
+                        }
+                        cnt = lo * HG;
+                    } else {
+                        cnt = s_nq[e] * HG;
+                    }
+                }
+                int incl = cnt;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(incl, o);
+                    if (lane >= o) incl += y;
+                }
+                if (e < nent) s_pre[e] = run + incl - cnt;
+                run += __shfl(incl, 63);
+            }
+            if (lane == 0) s_pre[nent] = run;
+        }
+        __syncthreads();
+        const uint32_t n_items = (uint32_t)s_pre[nent];
+        uint32_t c = s_claim;
+        while (c < n_items) {
+            // the entry e with s_pre[e] <= c < s_pre[e + 1]
+            int lo = 0, hi = nent;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if ((uint32_t)s_pre[mid] <= c) lo = mid; else hi = mid;
+            }
+            const int rem = (int)(c - (uint32_t)s_pre[lo]);
+            int lp, qt, hg;
+            if (a.by_rank) {
+                qt = qblocks - 1 - lo;
+                lp = s_lp[rem / HG];
+                hg = rem % HG;
+            } else {
+                lp = s_lp[lo];
+                qt = s_nq[lo] - 1 - rem / HG;
+                hg = rem % HG;
+            }
+            next_claim = 0xffffffffu;
+            run_item(__builtin_amdgcn_readfirstlane(8 * lp + xcd), __builtin_amdgcn_readfirstlane(qt),
+                     __builtin_amdgcn_readfirstlane(hg));
+            __syncthreads();   // every wave is past the item (its LDS is free) and has read c
+            if (tid == 0) {
+                // an item that left early (bad metadata) made no claim yet
+                if (next_claim == 0xffffffffu)
+                    next_claim = __hip_atomic_fetch_add(claim_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_claim = next_claim;
+            }
+            __syncthreads();
+            c = s_claim;
+        }
+        if (tid == 0) {
+            const uint32_t d = __hip_atomic_fetch_add(ctr + 8, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == gridDim.x - 1) {
+                // every workgroup has made its last claim: reset for the next call
+#pragma unroll
+                for (int x = 0; x < 9; ++x)
+                    __hip_atomic_store(ctr + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
 }
 
@@ -520,6 +681,20 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a) {
     for (int e = 0; e < EPL; ++e) pf_store<T>(o, lane * EPL + e, acc[e] * inv);
 }
 
+// Compute units of the current device (cached per device).
+static int prefill_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
     if (a.num_seqs == 0 || a.max_seqlen_q == 0) return hipSuccess;
     // The MFMA kernel's direct tile loads address up to 64 key rows per
@@ -530,17 +705,41 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
         // Four waves of 32 query rows per workgroup (one head, 128 rows), two
         // waves per SIMD: while one wave waits on LDS or runs its softmax the
         // other keeps the matrix core busy.
-        constexpr int NW = 4, RB = 1, BM = 32 * NW * RB;
+        constexpr int NW = 4, RB = 1;
+        // Keys read through block tables (prefix hits): two query heads of a
+        // GQA group share the workgroup (64 rows each) and every K/V tile it
+        // stages, which halves the tile loads and the block-table reads per
+        // query row. Contiguous keys: one head per workgroup, 128 rows; there
+        // the shorter query blocks cost more than the shared loads save.
+        const int hpw = a.paged && a.group % 2 == 0 ? 2 : 1;
+        const int bm = 32 * RB * (NW / hpw);
         const int64_t pairs = (int64_t)a.num_seqs * a.Hkv;
-        const int64_t nwg = 8 * ((pairs + 7) / 8) * ((a.max_seqlen_q + BM - 1) / BM) * a.group;
+        const int64_t qblocks = (a.max_seqlen_q + bm - 1) / bm;
+        // The persistent grid (two workgroups per CU claiming items) only when
+        // the caller gave a workspace and the item tables fit in LDS.
+        const bool persist = a.work_ctr != nullptr && (pairs + 7) / 8 <= kPfMaxXcdPairs &&
+                             qblocks <= kPfMaxQblocks;
+        int64_t nwg = 8 * ((pairs + 7) / 8) * qblocks * (a.group / hpw);
+        if (persist) nwg = 8 * ((2 * prefill_cus() + 7) / 8);
         if (nwg > 0x7fffffff) return hipErrorInvalidValue;
         const dim3 grid((unsigned)nwg), block(64 * NW);
-        if (!a.paged)
-            hipLaunchKernelGGL((prefill_mfma_kernel<kContiguous, NW, RB, 2>), grid, block, 0, stream, a);
-        else if (a.bs % kPfBN == 0)
-            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolBlocks, NW, RB, 2>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2>), grid, block, 0, stream, a);
+#define PKV_MFMA_LAUNCH(HPW, P)                                                                                \
+    do {                                                                                                       \
+        if (!a.paged)                                                                                          \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kContiguous, NW, RB, 2, HPW, P>), grid, block, 0, stream, a); \
+        else if (a.bs % kPfBN == 0)                                                                            \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolBlocks, NW, RB, 2, HPW, P>), grid, block, 0, stream, a); \
+        else                                                                                                   \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2, HPW, P>), grid, block, 0, stream, a);  \
+    } while (0)
+        if (persist) {
+            if (hpw == 2) PKV_MFMA_LAUNCH(2, true);
+            else PKV_MFMA_LAUNCH(1, true);
+        } else {
+            if (hpw == 2) PKV_MFMA_LAUNCH(2, false);
+            else PKV_MFMA_LAUNCH(1, false);
+        }
+#undef PKV_MFMA_LAUNCH
     } else {
         const dim3 grid((a.max_seqlen_q + 3) / 4, a.Hq, a.num_seqs);
         if (dtype == 0 && a.d == 64)

@@ -147,8 +147,9 @@ def test_device_calls_validate_before_launch():
                                       96, 1.0, 1, None, 0, None, 0, None)
     assert rc == 2
     rc = L.pkv_prefill_attention_varlen(None, 512, None, None, 0, None, None, None, 0, None, None,
-                                        0, 0, 0, 0, 0, 1, 4, 2, 64, 1.0, 0, None, None)
+                                        0, 0, 0, 0, 0, 1, 4, 2, 64, 1.0, 0, None, None, 0, None)
     assert rc == 0   # empty batch is a no-op
+    assert L.pkv_prefill_workspace_bytes(16, 2048, 16, 8, 128, 1) == 256
     rc = L.pkv_store_kvcache(None, None, 128, 128, None, None, None, 0, 4, 16, 2, 64, 0, None)
     assert rc == 0   # zero tokens is a no-op
 
