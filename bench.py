@@ -655,6 +655,7 @@ def summarize_trace(trace_dir, workload, steps, warmup, command):
     out = [f"Command: `{command}`", "",
            "| Kernel | Workload | Dispatches (timed) | Mean us | Median us | Min us | Max us |",
            "|---|---|---|---|---|---|---|"]
+    first = []   # (start, part, pass) of each step's first attention dispatch
     for phase, kernels in TRACE_KERNELS.items():
         mine = [p for p in parts if p[0] == phase]
         if not mine:
@@ -672,6 +673,25 @@ def summarize_trace(trace_dir, workload, steps, warmup, command):
                 d = [t for t, (pp, pas) in zip(durs, order) if pp == p and pas != "warmup"]
                 out.append(f"| {k} | {names.get(p[1], p[1])} (preset {p[1]}) | {len(d)} | "
                            f"{np.mean(d):.1f} | {np.median(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+            if k == kernels[0]:
+                first += [(int(r["Start_Timestamp"]), p, pas) for r, (p, pas) in
+                          zip([r for r in rows if r["Kernel_Name"].split("(")[0].split("<")[0].endswith(k)],
+                              order)]
+    # the store of a step is the last store dispatch before that step's attention
+    stores = [r for r in rows if "store_kvcache_kernel" in r["Kernel_Name"]
+              and "rope" not in r["Kernel_Name"]]
+    starts = [int(r["Start_Timestamp"]) for r in stores]
+    per = {}
+    for t0, p, pas in sorted(first, key=lambda x: x[0]):
+        i = int(np.searchsorted(starts, t0)) - 1
+        if i >= 0 and pas != "warmup":
+            r = stores[i]
+            per.setdefault(p, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    for p in parts:
+        d = per.get(p)
+        if d:
+            out.append(f"| store_kvcache_kernel | {names.get(p[1], p[1])} (preset {p[1]}) | {len(d)} | "
+                       f"{np.mean(d):.1f} | {np.median(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
     print("\n".join(out))
 
 

@@ -72,6 +72,11 @@ __device__ __forceinline__ int tile_swz(int t) { return ((t & 3) << 2) | ((t >> 
 
 // NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
 // owns BM = 32 * RB * NW rows of one query head. WPE waves share one SIMD.
+// Maximum of three scores (IEEE maximum, one v_maximum3_f32).
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 template <int SRC, int NW, int RB, int WPE, int HPW, bool PERSIST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_mfma_kernel(PrefillArgs a) {
@@ -317,17 +322,21 @@ void prefill_mfma_kernel(PrefillArgs a) {
                         for (int r = 0; r < 16; ++r)
                             st[rb][mt][r] = (32 * mt + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : st[rb][mt][r];
                 }
-                // four independent partial maxima, then a short tree
+                // four independent partial maxima, then a short tree. IEEE
+                // maximum (NaN-propagating) pairs into v_maximum3_f32 and,
+                // unlike fmaxf, needs no quieting of its inputs first.
                 float xq[4];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int mt = g >> 1, r0 = 8 * (g & 1);
-                    xq[g] = fmaxf(fmaxf(st[rb][mt][r0], st[rb][mt][r0 + 1]), st[rb][mt][r0 + 2]);
-                    xq[g] = fmaxf(fmaxf(xq[g], st[rb][mt][r0 + 3]), st[rb][mt][r0 + 4]);
-                    xq[g] = fmaxf(fmaxf(xq[g], st[rb][mt][r0 + 5]), st[rb][mt][r0 + 6]);
-                    xq[g] = fmaxf(xq[g], st[rb][mt][r0 + 7]);
+                    xq[g] = fmax3(st[rb][mt][r0], st[rb][mt][r0 + 1], st[rb][mt][r0 + 2]);
+                    xq[g] = fmax3(xq[g], st[rb][mt][r0 + 3], st[rb][mt][r0 + 4]);
+                    xq[g] = fmax3(xq[g], st[rb][mt][r0 + 5], st[rb][mt][r0 + 6]);
+                    xq[g] = fmax3(xq[g], st[rb][mt][r0 + 7], xq[g]);
                 }
-                mx[rb] = xor32_max(fmaxf(fmaxf(xq[0], xq[1]), fmaxf(xq[2], xq[3])));
+                const float x4 = fmax3(fmax3(xq[0], xq[1], xq[2]), xq[3], xq[3]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x4), __float_as_uint(x4), false, false);
+                mx[rb] = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
             bool grow = false;
 #pragma unroll
@@ -392,17 +401,29 @@ void prefill_mfma_kernel(PrefillArgs a) {
     load_tile(0, lds[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // Tiles below every row's diagonal need no mask; the last few do.
-    const int n_full = min(n_kt, max(0, (off + q0 + 1) / kPfBN));
+    // Tiles below the diagonal of every row of this wave need no mask; the
+    // last few do. Waves of one workgroup may split the tiles differently:
+    // every wave still passes one barrier per tile, and a barrier counts
+    // arrivals whatever instruction a wave reached it at.
+    const int n_full = min(n_kt, max(0, (off + q0 + 32 * RB * wh + 1) / kPfBN));
+    // Unrolled by two, so that each step's buffer is a constant and the
+    // operand read addresses need no per-tile arithmetic. The other buffer
+    // was last read before the previous barrier; the next tile's direct loads
+    // must have landed before the barrier hands its buffer to the other waves.
     int kt = 0;
-    for (; kt < n_full; ++kt) {
-        const int buf = kt & 1;
-        // The other buffer was last read before the previous barrier.
-        tile_step(std::false_type{}, lds[buf], lds[buf ^ 1], kt * kPfBN, kt + 1 < n_kt);
-        // The next tile's direct loads must have landed before the barrier
-        // hands its buffer to the other wave.
+    for (; kt + 1 < n_full; kt += 2) {
+        tile_step(std::false_type{}, lds[0], lds[1], kt * kPfBN, true);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        tile_step(std::false_type{}, lds[1], lds[0], (kt + 1) * kPfBN, kt + 2 < n_kt);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    if (kt < n_full) {   // kt is even here
+        tile_step(std::false_type{}, lds[0], lds[1], kt * kPfBN, kt + 1 < n_kt);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        ++kt;
     }
     for (; kt < n_kt; ++kt) {
         const int buf = kt & 1;

@@ -10,7 +10,7 @@
 // and of the V row is one work item. Consecutive lanes take consecutive chunks
 // of one row, so each wave instruction moves whole 64-byte segments; every
 // thread keeps kStoreUnroll items (2 * kStoreUnroll loads) in flight before
-// its stores. The K/V loads do not wait for the slot: they are issued with
+// its stores. Workgroups of 1024 threads, one item each. The K/V loads do not wait for the slot: they are issued with
 // the slot load (every token row is readable), and only the stores depend on
 // it.
 #include "pkv_device.h"
@@ -18,11 +18,11 @@
 
 namespace pkv {
 
-constexpr int kStoreThreads = 256;
-// Items per thread: 2 measured best (varlen 16k tokens: 30.5 us; prefix step,
-// 49k tokens: 67.6 us, 5.96 TB/s); 4 left fewer, longer-lived waves and was
-// 7-11% slower.
-constexpr int kStoreUnroll = 2;
+// 1024 threads x 1 item measured best among 64..1024 threads x 1..4 items and
+// grid-stride forms (16k tokens: 24.6 us against 25.2 for 256 x 2; 49k
+// tokens: 77.8 against 79.4); 4 items per thread were the slowest.
+constexpr int kStoreThreads = 1024;
+constexpr int kStoreUnroll = 1;
 
 __global__ __launch_bounds__(kStoreThreads) void store_kvcache_kernel(StoreArgs a) {
     const int64_t total = (int64_t)a.num_tokens * a.chunks_per_row;
