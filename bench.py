@@ -25,7 +25,9 @@ MFMA peak sit beside it. Each call is timed with HIP events on the stream it
 runs on. Several copies of the inputs are used in rotation so that no step
 finds its data in the 256 MB last-level cache. A read-only streaming kernel
 (libpkv_probe) is timed on a 2 GiB buffer in the same run, as an achievable
-reference beside the published HBM peak.
+reference beside the published HBM peak, and at each part's own byte counts
+a decode-shaped read (decode calls under 2 GiB) and a device copy (stores), so
+that short calls have a reference that pays the same launch ramp and drain.
 
 `--workload` selects other combinations (see WORKLOADS).
 """
@@ -58,6 +60,8 @@ WORKLOADS = {
     "prefill": [("prefill", 3)],
     "decode-long": [("decode", 5)],
     "prefill-prefix": [("prefill", 4)],
+    # the two parts the headline figures come from
+    "headline": [("decode", 5), ("prefill", 4)],
     # decode rows through the varlen prefill call, beside the decode kernel on
     # the same batch; and a mixed step (decode rows + two prompt chunks)
     "decode-in-varlen": [("decode", 2), ("prefill", 6)],
@@ -543,6 +547,64 @@ def stream_read_rates(reps: int = 5) -> dict:
     return out
 
 
+def size_matched_rates(parts, summaries, per_cu: int, cycles: int, reps: int = 20) -> dict:
+    """Plain data movement of each part's own byte counts, every launch alone
+    between two events behind a spin kernel (as the timed pass times the
+    attention and store calls), over as many rotating buffers as the part
+    keeps input copies: a decode-shaped read-only stream of a decode call's
+    bytes (parts under 2 GiB), and a device-to-device copy of a store's bytes.
+    What streaming itself reaches at that size, launch ramp and drain
+    included. Returns {workload: {...}}."""
+    import ctypes
+    from paged_kv_cache_125_amd.build import PROBE_LIB
+    L = ctypes.CDLL(PROBE_LIB)
+    L.pkv_probe_stream_read.restype = ctypes.c_int
+    L.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+
+    def timed(launch):
+        launch(0)                       # warm
+        torch.cuda.synchronize()
+        torch.cuda._sleep(cycles)
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            launch(i)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) * 1e-3 for a, b in ev]))
+
+    out = {}
+    for p, sm in zip(parts, summaries):
+        rec = {}
+        n = len(p.copies)
+        if p.phase == "decode" and sm["attention_bytes"] < STREAM_BYTES:
+            nb = int(-(-sm["attention_bytes"] // 2048) * 2048)
+            bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(0x5A + i) for i in range(n)]
+            t = timed(lambda i: L.pkv_probe_stream_read(ctypes.c_void_p(bufs[i % n].data_ptr()), nb, 1, 2048,
+                                                        cus * per_cu, ctypes.c_void_p(sink.data_ptr()), stream))
+            rec["stream_read"] = {"bytes": nb, "us": t * 1e6, "GBps": nb / t / 1e9,
+                                  "attention_over_stream": sm["attention_GBps"] / (nb / t / 1e9)}
+            del bufs
+        sb = rope_store_bytes(p.w) if p.rope else store_bytes(p.w)
+        half = int(sb // 2)
+        # sources and destinations both rotate, as the store's inputs and
+        # pools do, so the copy finds no more of its data in the MALL than
+        # the store does
+        srcs = [torch.empty(half, dtype=torch.uint8, device="cuda").fill_(0x33 + i) for i in range(n)]
+        dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        t = timed(lambda i: dsts[i % n].copy_(srcs[i % n]))
+        rec["device_copy"] = {"bytes": 2 * half, "us": t * 1e6, "GBps": 2 * half / t / 1e9,
+                              "store_over_copy": sm["store_GBps"] / (2 * half / t / 1e9)}
+        del srcs, dsts
+        torch.cuda.empty_cache()
+        out[sm["workload"]] = rec
+    return out
+
+
 def _source_sha(kernel_file: str) -> str:
     src = os.path.join(ROOT, "paged_kv_cache_125_amd", "csrc", kernel_file)
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -625,6 +687,33 @@ def summarize_counters(fetch_dir, write_dir, workload):
     os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
     json.dump(data, open(COUNTERS_JSON, "w"), indent=1, sort_keys=True)
     print(json.dumps({k: data[k]["hbm_bytes_per_launch"] for k in sorted(data)}, indent=1))
+
+
+def summarize_pmc(pmc_dir, command):
+    """Mean per dispatch of every counter of a rocprofv3 --pmc run, by
+    kernel, as markdown. With SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE in
+    the run, also the matrix cores' busy share: busy cycles summed over the
+    SIMDs / (SIMDs x active cycles per XCD; GRBM_GUI_ACTIVE sums the 8 XCDs)."""
+    tab = _read_counter_csvs(pmc_dir)
+    if not tab:
+        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
+    counters = sorted({c for v in tab.values() for c in v})
+    simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 1024
+    out = [f"Command: `{command}`", "",
+           "| Kernel | Dispatches | " + " | ".join(counters) + " | MFMA busy |",
+           "|---|---|" + "---|" * len(counters) + "---|"]
+    for k in sorted(tab, key=lambda n: -sum(sum(v) for v in tab[n].values())):
+        short = k.split("(")[0].replace("void ", "")
+        if not any(t in short for t in ("pkv::", "copyBuffer")):
+            continue
+        c = tab[k]
+        n = max(len(v) for v in c.values())
+        means = [float(np.mean(c[x])) if c.get(x) else float("nan") for x in counters]
+        busy = ""
+        if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and c.get("GRBM_GUI_ACTIVE"):
+            busy = f"{np.mean(c['SQ_VALU_MFMA_BUSY_CYCLES']) / (simds * np.mean(c['GRBM_GUI_ACTIVE']) / 8):.3f}"
+        out.append(f"| `{short}` | {n} | " + " | ".join(f"{m:.4g}" for m in means) + f" | {busy} |")
+    print("\n".join(out))
 
 
 # ----------------------------------------------------------------- kernel trace
@@ -728,6 +817,8 @@ def main():
                     help="first run a plain 1 GiB device copy (scales the HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs into profiles/counters.json and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("PMC_DIR", "COMMAND"),
+                    help="per-kernel means of a rocprofv3 --pmc run, then exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
                     help="per-workload kernel durations of a rocprofv3 --kernel-trace run of "
                          "the bench with the same --workload/--steps/--warmup, then exit")
@@ -737,6 +828,9 @@ def main():
             raise SystemExit("counter runs need a workload with one part per phase "
                              "(the counters are averaged per kernel name)")
         summarize_counters(*args.summarize_counters, args.workload)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.workload, args.steps, args.warmup,
@@ -843,6 +937,9 @@ def main():
         p.collect([events[i][j] for i in range(args.steps)])
     summaries = [p.summary() for p in parts]
     log("[bench] " + json.dumps(summaries))
+    log("[bench] size-matched streaming references")
+    size_matched = size_matched_rates(parts, summaries, stream_read["decode_shaped"]["workgroups_per_cu"],
+                                      preroll_cycles(5e-3))
 
     cpu = {}
     if not args.no_cpu_baseline:
@@ -930,6 +1027,7 @@ def main():
     # what plain streaming kernels reach on this GPU, beside the published peak
     sec["device_copy_GBps"] = copy_gbps
     sec["stream_read"] = stream_read
+    sec["size_matched"] = size_matched
     print(json.dumps(line), flush=True)
 
 
