@@ -179,7 +179,25 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const uint8_t *kbase = (const uint8_t *)(SRC == kContiguous ? a.k : a.kc) + (int64_t)kvh * kPfD * 2;
     const uint8_t *vbase = (const uint8_t *)(SRC == kContiguous ? a.v : a.vc) + (int64_t)kvh * kPfD * 2;
     const uint32_t stride_b = (uint32_t)(SRC == kContiguous ? a.kv_stride * 2 : (int64_t)a.Hkv * kPfD * 2);
-    const int32_t *bt_row = a.bt + (int64_t)s * a.maxb;
+    // Block-table entries are read through the scalar cache (a wave-uniform
+    // index) one tile ahead of the loads that use them: a vector load here
+    // would make every tile step wait for it (vmcnt counts in order) before
+    // it could issue the next tile's loads.
+    typedef const __attribute__((address_space(4))) int32_t *bt_ptr;
+    const bt_ptr bt_row = (bt_ptr)(a.bt + (int64_t)s * a.maxb);
+    auto blk_of = [&](int key0) -> int {   // block holding key key0; -1 past the keys or the table
+        const int lb = key0 >> a.log2bs;
+        return (key0 < kend && lb < a.maxb) ? bt_row[lb] : -1;
+    };
+    int pre_blk[8];   // block ids for the next load_tile: entry 0 (whole tiles) or LPW entries (small blocks)
+    auto fetch_blocks = [&](int k0) {
+        if constexpr (SRC == kPoolBlocks) {
+            pre_blk[0] = blk_of(k0);
+        } else if constexpr (SRC == kPoolSmall) {
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) pre_blk[i] = blk_of(k0 + 4 * (LPW * wave + i));
+        }
+    };
     int voff[8];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -195,8 +213,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
                 const int key0 = k0 + 4 * (LPW * wave + i);
-                const int lb = key0 >> a.log2bs;
-                const int blk = (key0 < kend && lb < a.maxb) ? bt_row[lb] : -1;
+                const int blk = pre_blk[i];
                 const bool ok = blk >= 0 && blk < a.num_blocks;
                 const int nrec = ok ? min(4, kend - key0) * (int)stride_b : 0;
                 const int64_t rb_ = ok ? ((int64_t)blk * a.bs + (key0 & (a.bs - 1))) * stride_b : 0;
@@ -212,8 +229,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
             if constexpr (SRC == kContiguous) {
                 row0 = (int64_t)k_start + k0;
             } else {
-                const int lb = k0 >> a.log2bs;
-                const int blk = (ok && lb < a.maxb) ? bt_row[lb] : -1;
+                const int blk = pre_blk[0];
                 ok = ok && blk >= 0 && blk < a.num_blocks;
                 row0 = (int64_t)blk * a.bs + (k0 & (a.bs - 1));
             }
@@ -396,9 +412,15 @@ void prefill_mfma_kernel(PrefillArgs a) {
                     }
                 }
         }
+        // the block ids of the tile after next, behind this step's LDS reads
+        // (a scalar load shares their counter); the wait before the barrier
+        // covers it
+        if (more) fetch_blocks(k0 + 2 * kPfBN);
     };
 
+    fetch_blocks(0);
     load_tile(0, lds[0]);
+    fetch_blocks(kPfBN);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Tiles below the diagonal of every row of this wave need no mask; the
