@@ -127,10 +127,29 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int s = pair / a.Hkv;
     const int kvh = pair - s * a.Hkv;
     const int h = kvh * a.group + hg * HPW + hh;
+    // Block-table entries are read through the scalar cache (a wave-uniform
+    // index) one tile ahead of the loads that use them: a vector load here
+    // would make every tile step wait for it (vmcnt counts in order) before
+    // it could issue the next tile's loads. The first tile's entries go out
+    // with the sequence bounds, before the key count is known (any entry of
+    // the sequence's table row may be read), and count only for keys that
+    // exist.
+    typedef const __attribute__((address_space(4))) int32_t *bt_ptr;
+    const bt_ptr bt_row = (bt_ptr)(a.bt + (int64_t)s * a.maxb);
+    constexpr int NB = SRC == kPoolSmall ? LPW : 1;   // block ids per wave and tile
+    auto key_of = [&](int k0, int i) { return SRC == kPoolSmall ? k0 + 4 * (LPW * wave + i) : k0; };
     // All four bounds in one round trip (a workgroup with no rows here
     // learns it from the first two and leaves).
     const int q_start = a.cu_q[s], q_end = a.cu_q[s + 1];
     const int k_start = a.cu_k[s], k_end = a.cu_k[s + 1];
+    int first_blk[8];
+    if constexpr (SRC != kContiguous) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int lb = key_of(0, i) >> a.log2bs;
+            first_blk[i] = lb < a.maxb ? bt_row[lb] : -1;
+        }
+    }
     const int Lq = q_end - q_start, Lk = k_end - k_start;
     const int q0 = qt * BM;
     // One test, so that the four loads above issue together. Rows outside
@@ -179,23 +198,15 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const uint8_t *kbase = (const uint8_t *)(SRC == kContiguous ? a.k : a.kc) + (int64_t)kvh * kPfD * 2;
     const uint8_t *vbase = (const uint8_t *)(SRC == kContiguous ? a.v : a.vc) + (int64_t)kvh * kPfD * 2;
     const uint32_t stride_b = (uint32_t)(SRC == kContiguous ? a.kv_stride * 2 : (int64_t)a.Hkv * kPfD * 2);
-    // Block-table entries are read through the scalar cache (a wave-uniform
-    // index) one tile ahead of the loads that use them: a vector load here
-    // would make every tile step wait for it (vmcnt counts in order) before
-    // it could issue the next tile's loads.
-    typedef const __attribute__((address_space(4))) int32_t *bt_ptr;
-    const bt_ptr bt_row = (bt_ptr)(a.bt + (int64_t)s * a.maxb);
     auto blk_of = [&](int key0) -> int {   // block holding key key0; -1 past the keys or the table
         const int lb = key0 >> a.log2bs;
         return (key0 < kend && lb < a.maxb) ? bt_row[lb] : -1;
     };
-    int pre_blk[8];   // block ids for the next load_tile: entry 0 (whole tiles) or LPW entries (small blocks)
+    int pre_blk[8];   // block ids for the next load_tile: NB entries
     auto fetch_blocks = [&](int k0) {
-        if constexpr (SRC == kPoolBlocks) {
-            pre_blk[0] = blk_of(k0);
-        } else if constexpr (SRC == kPoolSmall) {
+        if constexpr (SRC != kContiguous) {
 #pragma unroll
-            for (int i = 0; i < LPW; ++i) pre_blk[i] = blk_of(k0 + 4 * (LPW * wave + i));
+            for (int i = 0; i < NB; ++i) pre_blk[i] = blk_of(key_of(k0, i));
         }
     };
     int voff[8];
@@ -418,7 +429,10 @@ void prefill_mfma_kernel(PrefillArgs a) {
         if (more) fetch_blocks(k0 + 2 * kPfBN);
     };
 
-    fetch_blocks(0);
+    if constexpr (SRC != kContiguous) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) pre_blk[i] = key_of(0, i) < kend ? first_blk[i] : -1;
+    }
     load_tile(0, lds[0]);
     fetch_blocks(kPfBN);
     __builtin_amdgcn_s_waitcnt(0);
