@@ -94,7 +94,13 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // first RB (LPW) entries are ever touched.
     // Two buffers, each a K tile followed by a V tile, 64 keys x 256 bytes each.
     constexpr int kTileBytes = kPfBN * 256;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * kTileBytes];
+    // One LDS object: the tile buffers, then (persistent grid) its item
+    // tables. With the tables in objects of their own the compiler stopped
+    // telling the direct tile loads apart from the operand reads of the other
+    // buffer, and waited for every load before each tile's reads.
+    constexpr int kTabWords = PERSIST ? 3 * 256 + 512 + 2 : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_all[2 * 2 * kTileBytes + 4 * kTabWords];
+    auto lds = reinterpret_cast<uint8_t (*)[2 * kTileBytes]>(lds_all);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -563,11 +569,13 @@ void prefill_mfma_kernel(PrefillArgs a) {
         // LDS from cu_seqlens_q. An item's successor is claimed when its tile
         // loop is done. A workgroup leaves when its claim passes the end of
         // the list; the last one to leave zeroes the counters for the next call.
-        __shared__ int32_t s_nq[kPfMaxXcdPairs];      // query blocks per pair, sorted descending
-        __shared__ int32_t s_lp[kPfMaxXcdPairs];      // the pair (lp) at each sorted position
-        __shared__ int32_t s_raw[kPfMaxXcdPairs];     // query blocks per pair, by lp
-        __shared__ int32_t s_pre[kPfMaxQblocks + 1];  // items before rank r (or before sorted pair i)
-        __shared__ uint32_t s_claim;
+        static_assert(kPfMaxXcdPairs == 256 && kPfMaxQblocks == 512, "table sizes");
+        int32_t *const tab = reinterpret_cast<int32_t *>(lds_all + 2 * 2 * kTileBytes);
+        int32_t *const s_nq = tab;                    // query blocks per pair, sorted descending
+        int32_t *const s_lp = tab + 256;              // the pair (lp) at each sorted position
+        int32_t *const s_raw = tab + 512;             // query blocks per pair, by lp
+        int32_t *const s_pre = tab + 768;             // items before rank r (or before sorted pair i)
+        uint32_t &s_claim = *reinterpret_cast<uint32_t *>(tab + 768 + 513);
         uint32_t *ctr = a.work_ctr;
         const int npx = (npairs + 7 - xcd) / 8;       // pairs of this XCD: lp < npx
         for (int lp = tid; lp < npx; lp += 64 * NW) {
