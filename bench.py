@@ -547,6 +547,56 @@ def stream_read_rates(reps: int = 5) -> dict:
     return out
 
 
+ISSUE_MODES = {   # mode: (what one pass issues, instructions the rate is per)
+    0: ("16 ds_read_b128, K-operand addresses", 16), 1: ("32 ds_read_b64_tr_b16, V^T addresses", 32),
+    2: ("16 v_mfma_f32_32x32x16_bf16", 16), 3: ("32 v_exp_f32", 32), 4: ("32 v_fma_f32", 32),
+    5: ("16 x (MFMA + 1 K read), per MFMA", 16), 6: ("16 x (MFMA + 2 V^T reads), per MFMA", 16),
+    7: ("16 MFMA + 24 reads (tile mix), per MFMA", 16)}
+
+
+def issue_rates() -> str:
+    """libpkv_probe's issue-rate probes (pkv_probe_issue) as markdown: cycles
+    per instruction per SIMD (the slowest wave of each CU's workgroup, over
+    all the instructions its SIMD's waves issued) and per wave, at 1, 2 and 4
+    waves per SIMD; then one MFMA wave and one VALU wave per SIMD, alone and
+    together."""
+    import ctypes
+    from paged_kv_cache_125_amd.build import PROBE_LIB
+    L = ctypes.CDLL(PROBE_LIB)
+    L.pkv_probe_issue.restype = ctypes.c_int
+    L.pkv_probe_issue.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cyc = torch.zeros(cus * 16, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    passes = 64
+
+    def run(mode, wps):
+        for _ in range(2):   # the first launch loads the code
+            if L.pkv_probe_issue(mode, wps, cus, ctypes.c_void_p(cyc.data_ptr()),
+                                 ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+                raise RuntimeError(f"pkv_probe_issue mode {mode} failed")
+        torch.cuda.synchronize()
+        return cyc.view(cus, 16).cpu().numpy().astype(np.float64)
+
+    out = ["| Block | waves per SIMD | cycles per instruction per SIMD | per wave |", "|---|---|---|---|"]
+    for mode, (name, n) in ISSUE_MODES.items():
+        # (at 4 waves per SIMD modes 5 and 6 exceed their 128 registers and spill)
+        for wps in ((1, 2) if mode in (5, 6) else (1, 2, 4)):
+            c = run(mode, wps)[:, :4 * wps]
+            per_simd = c.max(axis=1).mean() / (passes * n * wps)
+            out.append(f"| {name} | {wps} | {per_simd:.1f} | {c.mean() / (passes * n):.1f} |")
+    out += ["", "| One MFMA wave and one VALU wave per SIMD | MFMA wave: cycles per pass (16 MFMAs) | "
+            "VALU wave: cycles per pass (32 exp + 32 fma) |", "|---|---|---|"]
+    for mode, name in ((9, "MFMA waves alone"), (10, "VALU waves alone"), (8, "both")):
+        c = run(mode, 2)
+        a = c[:, :4].max(axis=1).mean() / passes if mode != 10 else float("nan")
+        b = c[:, 4:8].max(axis=1).mean() / passes if mode != 9 else float("nan")
+        out.append(f"| {name} | {a:.0f} | {b:.0f} |")
+    return "\n".join(out)
+
+
 def size_matched_rates(parts, summaries, per_cu: int, cycles: int, reps: int = 20) -> dict:
     """Plain data movement of each part's own byte counts, every launch alone
     between two events behind a spin kernel (as the timed pass times the
@@ -817,6 +867,8 @@ def main():
                     help="first run a plain 1 GiB device copy (scales the HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs into profiles/counters.json and exit")
+    ap.add_argument("--issue-rates", action="store_true",
+                    help="print the issue-rate probes (libpkv_probe) as markdown and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("PMC_DIR", "COMMAND"),
                     help="per-kernel means of a rocprofv3 --pmc run, then exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
@@ -845,6 +897,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.issue_rates:
+        print(issue_rates(), flush=True)
+        return
     import paged_kv_cache_125_amd as pkv
     pkv.lib()
 

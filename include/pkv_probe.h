@@ -32,6 +32,28 @@ extern "C" {
 int pkv_probe_stream_read(const void *buf, size_t bytes, int32_t mode, int32_t row_bytes,
                           int32_t blocks, int32_t *sink, void *stream);
 
+/* pkv_probe_issue times blocks of instructions as the prefill tile loop uses
+ * them, to show what bounds that loop: one workgroup of 4 * waves_per_simd
+ * waves per CU (its 96 KiB of LDS keeps a second workgroup off the CU), each
+ * wave running 64 passes of one block and storing its shader-clock cycles in
+ * cycles[block * 16 + wave] (device memory, blocks * 16 entries; entries of
+ * absent waves are left as they are).
+ *   mode 0  16 ds_read_b128 at the K-operand addresses (rows 256 B apart,
+ *           XOR swizzle), then a wait
+ *   mode 1  32 ds_read_b64_tr_b16 at the V^T-operand addresses, then a wait
+ *   mode 2  16 v_mfma_f32_32x32x16_bf16 on 4 accumulators
+ *   mode 3  32 independent v_exp_f32
+ *   mode 4  32 v_fma_f32 on 32 chains
+ *   mode 5  16 x (MFMA, one K-operand read); mode 6: 16 x (MFMA, two V^T
+ *           reads); mode 7: 16 MFMAs with 24 reads, the tile's mix
+ *   mode 8  waves 0-3 run 16 MFMAs while waves 4-7 (one beside each) run
+ *           32 exp + 32 fma; mode 9: waves 0-3 alone; mode 10: waves 4-7
+ *           alone (modes 8-10 need waves_per_simd 2)
+ * waves_per_simd is 1, 2 or 4. Returns 0, 1 for bad arguments, 3 when the
+ * launch fails. Asynchronous on `stream`. */
+int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blocks, uint64_t *cycles,
+                    int32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

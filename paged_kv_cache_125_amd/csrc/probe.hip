@@ -64,6 +64,160 @@ __global__ __launch_bounds__(256) void stream_read_rows(const uint8_t *buf, int6
     keep(acc, sink);
 }
 
+
+// ---------------------------------------------------------------------------
+// Issue-rate probes. One workgroup per CU (96 KiB of LDS keeps a second one
+// off), 4 * waves_per_simd waves, so wave w runs on SIMD w % 4 beside
+// waves_per_simd - 1 others. Every wave runs kIssuePasses passes of one block
+// of instructions (inline assembly, so the block is exactly what is timed)
+// and stores its shader-clock cycles in cycles[block * 16 + wave]. LDS
+// addresses stay inside the first 64 KiB of the array; results are folded
+// into a value that is stored only if it equals a fixed word.
+constexpr int kIssueLds = 96 * 1024;
+constexpr int kIssuePasses = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int tile_swz4(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+
+template <int MODE, int NT>
+__global__ __launch_bounds__(NT) void issue_probe(uint64_t *cycles, int32_t *sink) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kIssueLds];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kIssueLds / 16; i += blockDim.x)
+        *reinterpret_cast<u32x4 *>(lds + 16 * i) = u32x4{(uint32_t)i, (uint32_t)i * 3u, 7u, 9u};
+    __syncthreads();
+    // operand-read addresses of the prefill tile loop: K rows 256 B apart
+    // with the XOR swizzle, and the transposed V^T reads
+    const uint32_t base = (uint32_t)(uintptr_t)lds + (uint32_t)((wave & 3) * 16384);
+    const int r32 = lane & 31, j = lane >> 5, q16 = lane & 15, g2 = (lane >> 4) & 1;
+    uint32_t ak[8], av[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) ak[kk] = base + r32 * 256 + 16 * ((2 * kk + j) ^ tile_swz4(r32));
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int t = 4 * j + 8 * hi + (q16 >> 2);
+            const int chunk = 4 * nt + 2 * g2 + ((q16 & 3) >> 1);
+            av[hi][nt] = base + t * 256 + 16 * (chunk ^ tile_swz4(t)) + 8 * (q16 & 1);
+        }
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(0.01f * e);
+        b[e] = (__bf16)(0.02f * lane);
+    }
+    float x[32], y[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        x[k] = (lane + k) * 1e-3f;
+        y[k] = 0.f;
+    }
+    uint32_t fold = 0;
+    const bool group_a = wave < 4;
+    __syncthreads();
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < kIssuePasses; ++it) {
+        if constexpr (MODE == 0) {   // 16 K-operand reads
+            u32x4 v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v[k]) : "v"(ak[k >> 1]), "i"((k & 1) * 8192));
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int k = 0; k < 16; ++k) fold ^= v[k][0];
+        } else if constexpr (MODE == 1) {   // 32 transposed V^T reads
+            u32x2 v[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v[k]) : "v"(av[k & 1][(k >> 1) & 3]), "i"((k >> 3) * 4096));
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int k = 0; k < 32; ++k) fold ^= v[k][0];
+        } else if constexpr (MODE == 2) {   // 16 MFMAs
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[k & 3]) : "v"(a), "v"(b));
+        } else if constexpr (MODE == 3) {   // 32 independent exps
+#pragma unroll
+            for (int k = 0; k < 32; ++k) asm volatile("v_exp_f32 %0, %1" : "=v"(y[k]) : "v"(x[k]));
+        } else if constexpr (MODE == 4) {   // 32 fmas on 32 chains
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(y[k]) : "v"(x[k]), "v"(x[(k + 1) & 31]));
+        } else if constexpr (MODE >= 5 && MODE <= 7) {
+            // 16 MFMAs, each followed by operand reads: one K read (5), two
+            // V^T reads (6), or the tile's mix of 1.5 per MFMA (7)
+            u32x4 vb[16];
+            u32x2 vt[32];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[k & 3]) : "v"(a), "v"(b));
+                if constexpr (MODE == 5) {
+                    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(vb[k]) : "v"(ak[k >> 1]), "i"((k & 1) * 8192));
+                } else if constexpr (MODE == 6) {
+                    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vt[2 * k]) : "v"(av[0][k & 3]), "i"((k >> 2) * 4096));
+                    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vt[2 * k + 1]) : "v"(av[1][k & 3]), "i"((k >> 2) * 4096));
+                } else if (k & 1) {
+                    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vt[k]) : "v"(av[0][k & 3]), "i"((k >> 2) * 4096));
+                    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vt[k + 16]) : "v"(av[1][k & 3]), "i"((k >> 2) * 4096));
+                } else {
+                    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(vb[k]) : "v"(ak[k >> 1]), "i"((k & 1) * 8192));
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if constexpr (MODE == 5) fold ^= vb[k][2];
+                else if constexpr (MODE == 6) fold ^= vt[2 * k][1] ^ vt[2 * k + 1][0];
+                else fold ^= (k & 1) ? (vt[k][1] ^ vt[k + 16][0]) : vb[k][2];
+            }
+        } else {
+            // 8: group A (waves 0-3) 16 MFMAs, group B (waves 4-7, one on
+            // each SIMD beside an A wave) 32 exps + 32 fmas; 9: A alone;
+            // 10: B alone
+            if (group_a && MODE != 10) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[k & 3]) : "v"(a), "v"(b));
+            } else if (!group_a && MODE != 9) {
+#pragma unroll
+                for (int k = 0; k < 32; ++k) {
+                    asm volatile("v_exp_f32 %0, %1" : "=v"(y[k]) : "v"(x[k]));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x[k]) : "v"(y[(k + 1) & 31]), "v"(y[(k + 3) & 31]));
+                }
+            }
+        }
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    // every mode reads the LDS array, so that every mode allocates it
+    fold ^= *reinterpret_cast<const uint32_t *>(lds + 4 * (tid & 1023));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) fold ^= __float_as_uint(acc[i][r]);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) fold ^= __float_as_uint(y[k]) ^ __float_as_uint(x[k]);
+    if (fold == kMagic) sink[0] = (int32_t)blockIdx.x;
+    if (lane == 0) cycles[(int64_t)blockIdx.x * 16 + wave] = t1 - t0;
+}
+
+// The register budget follows the workgroup size (launch bounds per size).
+template <int MODE>
+hipError_t launch_issue(int32_t blocks, int32_t waves, uint64_t *cycles, int32_t *sink, hipStream_t s) {
+    if (waves == 4) hipLaunchKernelGGL((issue_probe<MODE, 256>), dim3(blocks), dim3(256), 0, s, cycles, sink);
+    else if (waves == 8) hipLaunchKernelGGL((issue_probe<MODE, 512>), dim3(blocks), dim3(512), 0, s, cycles, sink);
+    else hipLaunchKernelGGL((issue_probe<MODE, 1024>), dim3(blocks), dim3(1024), 0, s, cycles, sink);
+    return hipGetLastError();
+}
 }  // namespace
 
 extern "C" int pkv_probe_stream_read(const void *buf, size_t bytes, int32_t mode, int32_t row_bytes,
@@ -83,4 +237,28 @@ extern "C" int pkv_probe_stream_read(const void *buf, size_t bytes, int32_t mode
         return 1;
     }
     return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+extern "C" int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blocks, uint64_t *cycles,
+                               int32_t *sink, void *stream) {
+    if (!cycles || !sink || blocks <= 0 || mode < 0 || mode > 10) return 1;
+    if (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4) return 1;
+    if (mode >= 8 && waves_per_simd != 2) return 1;
+    const int32_t waves = 4 * waves_per_simd;
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipErrorInvalidValue;
+    switch (mode) {
+        case 0: e = launch_issue<0>(blocks, waves, cycles, sink, s); break;
+        case 1: e = launch_issue<1>(blocks, waves, cycles, sink, s); break;
+        case 2: e = launch_issue<2>(blocks, waves, cycles, sink, s); break;
+        case 3: e = launch_issue<3>(blocks, waves, cycles, sink, s); break;
+        case 4: e = launch_issue<4>(blocks, waves, cycles, sink, s); break;
+        case 5: e = launch_issue<5>(blocks, waves, cycles, sink, s); break;
+        case 6: e = launch_issue<6>(blocks, waves, cycles, sink, s); break;
+        case 7: e = launch_issue<7>(blocks, waves, cycles, sink, s); break;
+        case 8: e = launch_issue<8>(blocks, waves, cycles, sink, s); break;
+        case 9: e = launch_issue<9>(blocks, waves, cycles, sink, s); break;
+        case 10: e = launch_issue<10>(blocks, waves, cycles, sink, s); break;
+    }
+    return e == hipSuccess ? 0 : 3;
 }
