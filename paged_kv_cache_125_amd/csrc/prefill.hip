@@ -77,14 +77,10 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-template <int SRC, int NW, int RB, int WPE, int HPW, bool PERSIST>
+template <int SRC, int NW, int RB, int WPE, bool PERSIST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_mfma_kernel(PrefillArgs a) {
-    // HPW query heads of one kv head share the workgroup (and every K/V tile
-    // it stages); each head gets NW / HPW waves of RB blocks of 32 rows.
-    constexpr int WPH = NW / HPW;            // waves per head
-    constexpr int BM = 32 * RB * WPH;        // query rows per workgroup
-    static_assert(NW % HPW == 0, "heads must split the waves evenly");
+    constexpr int BM = 32 * RB * NW;         // query rows per workgroup (one query head)
     constexpr int LPW = 16 / NW;   // 1 KiB direct-load instructions per wave per K (or V) tile
     static_assert(NW * LPW == 16 && NW >= 2, "waves must split a tile evenly");
     static_assert(RB == 1 || RB == 2, "row blocks per wave");
@@ -116,11 +112,11 @@ void prefill_mfma_kernel(PrefillArgs a) {
     //    pairs' K/V are live at a time.
     // Either way the group's heads sit side by side and every (pair, query
     // block, head) is visited once.
-    const int HG = a.group / HPW;            // head groups per kv head
+    const int HG = a.group;                  // query heads per kv head
     const int qblocks = (a.max_seqlen_q + BM - 1) / BM;
     const int npairs = a.num_seqs * a.Hkv;
     const int xcd = blockIdx.x & 7;
-    const int hh = wave / WPH, wh = wave - hh * WPH;   // the wave's head in the group, its place in the head
+    const int wh = wave;                     // the wave's place in the workgroup's rows
 
     // Persistent grid: the claim of the next item, issued by thread 0 once an
     // item's tile loop is done (so that the per-tile waits for vector memory
@@ -132,7 +128,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     auto run_item = [&](const int pair, const int qt, const int hg) {
     const int s = pair / a.Hkv;
     const int kvh = pair - s * a.Hkv;
-    const int h = kvh * a.group + hg * HPW + hh;
+    const int h = kvh * a.group + hg;
     // Block-table entries are read through the scalar cache (a wave-uniform
     // index) one tile ahead of the loads that use them: a vector load here
     // would make every tile step wait for it (vmcnt counts in order) before
@@ -771,39 +767,31 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
         // waves per SIMD: while one wave waits on LDS or runs its softmax the
         // other keeps the matrix core busy.
         constexpr int NW = 4, RB = 1;
-        // Keys read through block tables (prefix hits): two query heads of a
-        // GQA group share the workgroup (64 rows each) and every K/V tile it
-        // stages, which halves the tile loads and the block-table reads per
-        // query row. Contiguous keys: one head per workgroup, 128 rows; there
-        // the shorter query blocks cost more than the shared loads save.
-        const int hpw = a.paged && a.group % 2 == 0 ? 2 : 1;
-        const int bm = 32 * RB * (NW / hpw);
+        // One query head per workgroup, 128 rows. (Two heads of a GQA group
+        // sharing a workgroup's K/V tiles, 64 rows each, measured equal on
+        // prefix hits and 9% slower on a mixed step once the block-table
+        // reads were taken off the tile loop's critical path.)
         const int64_t pairs = (int64_t)a.num_seqs * a.Hkv;
-        const int64_t qblocks = (a.max_seqlen_q + bm - 1) / bm;
+        const int64_t qblocks = (a.max_seqlen_q + 32 * RB * NW - 1) / (32 * RB * NW);
         // The persistent grid (two workgroups per CU claiming items) only when
         // the caller gave a workspace and the item tables fit in LDS.
         const bool persist = a.work_ctr != nullptr && (pairs + 7) / 8 <= kPfMaxXcdPairs &&
                              qblocks <= kPfMaxQblocks;
-        int64_t nwg = 8 * ((pairs + 7) / 8) * qblocks * (a.group / hpw);
+        int64_t nwg = 8 * ((pairs + 7) / 8) * qblocks * a.group;
         if (persist) nwg = 8 * ((2 * prefill_cus() + 7) / 8);
         if (nwg > 0x7fffffff) return hipErrorInvalidValue;
         const dim3 grid((unsigned)nwg), block(64 * NW);
-#define PKV_MFMA_LAUNCH(HPW, P)                                                                                \
-    do {                                                                                                       \
-        if (!a.paged)                                                                                          \
-            hipLaunchKernelGGL((prefill_mfma_kernel<kContiguous, NW, RB, 2, HPW, P>), grid, block, 0, stream, a); \
-        else if (a.bs % kPfBN == 0)                                                                            \
-            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolBlocks, NW, RB, 2, HPW, P>), grid, block, 0, stream, a); \
-        else                                                                                                   \
-            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2, HPW, P>), grid, block, 0, stream, a);  \
+#define PKV_MFMA_LAUNCH(P)                                                                                \
+    do {                                                                                                  \
+        if (!a.paged)                                                                                     \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kContiguous, NW, RB, 2, P>), grid, block, 0, stream, a); \
+        else if (a.bs % kPfBN == 0)                                                                       \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolBlocks, NW, RB, 2, P>), grid, block, 0, stream, a); \
+        else                                                                                              \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2, P>), grid, block, 0, stream, a);  \
     } while (0)
-        if (persist) {
-            if (hpw == 2) PKV_MFMA_LAUNCH(2, true);
-            else PKV_MFMA_LAUNCH(1, true);
-        } else {
-            if (hpw == 2) PKV_MFMA_LAUNCH(2, false);
-            else PKV_MFMA_LAUNCH(1, false);
-        }
+        if (persist) PKV_MFMA_LAUNCH(true);
+        else PKV_MFMA_LAUNCH(false);
 #undef PKV_MFMA_LAUNCH
     } else {
         const dim3 grid((a.max_seqlen_q + 3) / 4, a.Hq, a.num_seqs);
