@@ -70,13 +70,13 @@ enum KeySource {
 // has LDS bank conflicts.
 __device__ __forceinline__ int tile_swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
 
-// NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
-// owns BM = 32 * RB * NW rows of one query head. WPE waves share one SIMD.
 // Maximum of three scores (IEEE maximum, one v_maximum3_f32).
 __device__ __forceinline__ float fmax3(float a, float b, float c) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
+// NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
+// owns BM = 32 * RB * NW rows of one query head. WPE waves share one SIMD.
 template <int SRC, int NW, int RB, int WPE, bool PERSIST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_mfma_kernel(PrefillArgs a) {
