@@ -551,7 +551,11 @@ ISSUE_MODES = {   # mode: (what one pass issues, instructions the rate is per)
     0: ("16 ds_read_b128, K-operand addresses", 16), 1: ("32 ds_read_b64_tr_b16, V^T addresses", 32),
     2: ("16 v_mfma_f32_32x32x16_bf16", 16), 3: ("32 v_exp_f32", 32), 4: ("32 v_fma_f32", 32),
     5: ("16 x (MFMA + 1 K read), per MFMA", 16), 6: ("16 x (MFMA + 2 V^T reads), per MFMA", 16),
-    7: ("16 MFMA + 24 reads (tile mix), per MFMA", 16)}
+    7: ("16 MFMA + 24 reads (tile mix), per MFMA", 16),
+    11: ("16 x (MFMA + 4 fma, one wave), per MFMA", 16), 12: ("16 x (MFMA + 2 exp + 2 fma, one wave), per MFMA", 16),
+    13: ("16 x (MFMA + 8 fma, one wave), per MFMA", 16),
+    14: ("16 x (MFMA + 1.5 reads + 4 fma, one wave), per MFMA", 16),
+    15: ("16 x (MFMA + 1.5 reads + 2 exp + 2 fma, one wave), per MFMA", 16)}
 
 
 def issue_rates() -> str:
@@ -582,8 +586,8 @@ def issue_rates() -> str:
 
     out = ["| Block | waves per SIMD | cycles per instruction per SIMD | per wave |", "|---|---|---|---|"]
     for mode, (name, n) in ISSUE_MODES.items():
-        # (at 4 waves per SIMD modes 5 and 6 exceed their 128 registers and spill)
-        for wps in ((1, 2) if mode in (5, 6) else (1, 2, 4)):
+        # (at 4 waves per SIMD modes 5, 6 and 11-15 exceed their 128 registers and spill)
+        for wps in ((1, 2) if mode in (5, 6, 11, 12, 13, 14, 15) else (1, 2, 4)):
             c = run(mode, wps)[:, :4 * wps]
             per_simd = c.max(axis=1).mean() / (passes * n * wps)
             out.append(f"| {name} | {wps} | {per_simd:.1f} | {c.mean() / (passes * n):.1f} |")

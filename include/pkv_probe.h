@@ -49,6 +49,12 @@ int pkv_probe_stream_read(const void *buf, size_t bytes, int32_t mode, int32_t r
  *   mode 8  waves 0-3 run 16 MFMAs while waves 4-7 (one beside each) run
  *           32 exp + 32 fma; mode 9: waves 0-3 alone; mode 10: waves 4-7
  *           alone (modes 8-10 need waves_per_simd 2)
+ *   mode 11 16 x (MFMA, 4 independent v_fma_f32 of the same wave); mode 12:
+ *           16 x (MFMA, 2 v_exp_f32 + 2 v_fma_f32); mode 13: 16 x (MFMA,
+ *           8 v_fma_f32)
+ *   mode 14 the tile mix of one wave: 16 MFMAs, 24 operand reads (as mode
+ *           7) and 4 v_fma_f32 per MFMA; mode 15: the same with 2 v_exp_f32
+ *           + 2 v_fma_f32 per MFMA
  * waves_per_simd is 1, 2 or 4. Returns 0, 1 for bad arguments, 3 when the
  * launch fails. Asynchronous on `stream`. */
 int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blocks, uint64_t *cycles,

@@ -29,6 +29,7 @@
 #include <stdlib.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -73,6 +74,15 @@ __device__ __forceinline__ int tile_swz(int t) { return ((t & 3) << 2) | ((t >> 
 // Maximum of three scores (IEEE maximum, one v_maximum3_f32).
 __device__ __forceinline__ float fmax3(float a, float b, float c) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// A wave's direct loads of one tile operand from one descriptor: load i
+// lands 1024*i bytes past the LDS base d and reads 1024*i bytes past
+// voff[i] (the instruction offset moves both addresses).
+template <int... I>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __attribute__((address_space(3))) void *d,
+                                         const int (&voff)[8], std::integer_sequence<int, I...>) {
+    (__builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, voff[I], 0, 1024 * I, 0), ...);
 }
 
 // NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
@@ -196,7 +206,18 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // registers in between. Instruction i of wave w fills LDS bytes
     // [1024*(LPW*w+i), +1024) of a tile: keys 4*(LPW*w+i) + lane/16, chunk
     // position lane%16. Keys at or past kend are outside the descriptor's
-    // range and arrive as zeros.
+    // range and arrive as zeros; a tile wholly past them gets a zero record
+    // count, so the loads carry no branches (the step after the last tile
+    // loads nothing and writes zeros into a buffer no one reads). With one
+    // descriptor per tile, a wave's loads of one operand share one LDS base
+    // (M0) and step through the tile with the instruction offset 1024*i,
+    // which the hardware adds to both the LDS and the source address; it is
+    // taken out of the per-lane source offset, which stays non-negative
+    // since key rows are at least 256 bytes apart. Small blocks take one
+    // descriptor per 4 keys and an LDS base per load. Record counts go
+    // through readfirstlane: the clamps select to vector med3, and a
+    // descriptor word in a vector register would put every load in a loop
+    // over its distinct values.
     const uint8_t *kbase = (const uint8_t *)(SRC == kContiguous ? a.k : a.kc) + (int64_t)kvh * kPfD * 2;
     const uint8_t *vbase = (const uint8_t *)(SRC == kContiguous ? a.v : a.vc) + (int64_t)kvh * kPfD * 2;
     const uint32_t stride_b = (uint32_t)(SRC == kContiguous ? a.kv_stride * 2 : (int64_t)a.Hkv * kPfD * 2);
@@ -216,7 +237,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
     for (int i = 0; i < LPW; ++i) {
         const int t = 4 * (LPW * wave + i) + (lane >> 4);
         const int chunk = (lane & 15) ^ tile_swz(t);
-        voff[i] = (SRC == kPoolSmall ? (lane >> 4) : t) * (int)stride_b + 16 * chunk;
+        voff[i] = SRC == kPoolSmall ? (lane >> 4) * (int)stride_b + 16 * chunk
+                                    : t * (int)stride_b + 16 * chunk - 1024 * i;
     }
     typedef __attribute__((address_space(3))) void lds_t;
     auto load_tile = [&](int k0, uint8_t *dst) {
@@ -227,34 +249,31 @@ void prefill_mfma_kernel(PrefillArgs a) {
             for (int i = 0; i < LPW; ++i) {
                 const int key0 = k0 + 4 * (LPW * wave + i);
                 const int blk = pre_blk[i];
-                const bool ok = blk >= 0 && blk < a.num_blocks;
-                const int nrec = ok ? min(4, kend - key0) * (int)stride_b : 0;
-                const int64_t rb_ = ok ? ((int64_t)blk * a.bs + (key0 & (a.bs - 1))) * stride_b : 0;
+                const bool ok = (uint32_t)blk < (uint32_t)a.num_blocks;
+                const int nrec = __builtin_amdgcn_readfirstlane(ok ? min(4, max(0, kend - key0)) * (int)stride_b : 0);
+                const int64_t rb_ = ((int64_t)(ok ? blk : 0) * a.bs + (key0 & (a.bs - 1))) * stride_b;
                 const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + rb_), (short)0, nrec, kBufWord3);
                 const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + rb_), (short)0, nrec, kBufWord3);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_t *)(kd + 1024 * i), 16, voff[i], 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_t *)(vd + 1024 * i), 16, voff[i], 0, 0, 0);
             }
         } else {
-            const int valid = min(kPfBN, kend - k0);
+            const int nkeys = min(kPfBN, max(0, kend - k0));
             int64_t row0;   // first key row of the tile in its source
-            bool ok = valid > 0;
+            bool ok = true;
             if constexpr (SRC == kContiguous) {
                 row0 = (int64_t)k_start + k0;
             } else {
                 const int blk = pre_blk[0];
-                ok = ok && blk >= 0 && blk < a.num_blocks;
-                row0 = (int64_t)blk * a.bs + (k0 & (a.bs - 1));
+                ok = (uint32_t)blk < (uint32_t)a.num_blocks;
+                row0 = (int64_t)(ok ? blk : 0) * a.bs + (k0 & (a.bs - 1));
             }
-            const int nrec = ok ? valid * (int)stride_b : 0;
-            const int64_t rb_ = ok ? row0 * stride_b : 0;
+            const int nrec = __builtin_amdgcn_readfirstlane(ok ? nkeys * (int)stride_b : 0);
+            const int64_t rb_ = row0 * stride_b;
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + rb_), (short)0, nrec, kBufWord3);
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + rb_), (short)0, nrec, kBufWord3);
-#pragma unroll
-            for (int i = 0; i < LPW; ++i) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_t *)(kd + 1024 * i), 16, voff[i], 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_t *)(vd + 1024 * i), 16, voff[i], 0, 0, 0);
-            }
+            dma_tile(rk, (lds_t *)kd, voff, std::make_integer_sequence<int, LPW>{});
+            dma_tile(rv, (lds_t *)vd, voff, std::make_integer_sequence<int, LPW>{});
         }
     };
 
@@ -299,7 +318,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // lets the compiler read `cur` without waiting for the loads into `nxt`.
     auto tile_step = [&](auto masked, const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
                          int k0, bool more) {
-        if (more) load_tile(k0 + kPfBN, nxt);
+        load_tile(k0 + kPfBN, nxt);
         const uint8_t *Ks = cur;
         const uint8_t *Vs = cur + kTileBytes;
         if (wave_rows && (!decltype(masked)::value || k0 <= pos_last)) {

@@ -180,6 +180,53 @@ __global__ __launch_bounds__(NT) void issue_probe(uint64_t *cycles, int32_t *sin
                 else if constexpr (MODE == 6) fold ^= vt[2 * k][1] ^ vt[2 * k + 1][0];
                 else fold ^= (k & 1) ? (vt[k][1] ^ vt[k + 16][0]) : vb[k][2];
             }
+        } else if constexpr (MODE >= 14) {
+            // the whole tile mix in one wave: 16 MFMAs with 24 operand
+            // reads (as mode 7) and 4 fmas (14) or 2 exps + 2 fmas (15) each
+            u32x4 vb[8];
+            u32x2 vt[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[k & 3]) : "v"(a), "v"(b));
+                if (k & 1) {
+                    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vt[k - 1]) : "v"(av[0][k & 3]), "i"((k >> 2) * 4096));
+                    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vt[k]) : "v"(av[1][k & 3]), "i"((k >> 2) * 4096));
+                } else {
+                    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(vb[k >> 1]) : "v"(ak[k >> 1]), "i"(0));
+                }
+                if constexpr (MODE == 15) {
+                    asm volatile("v_exp_f32 %0, %1" : "=v"(y[(2 * k) & 31]) : "v"(x[(2 * k) & 31]));
+                    asm volatile("v_exp_f32 %0, %1" : "=v"(y[(2 * k + 1) & 31]) : "v"(x[(2 * k + 1) & 31]));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x[(2 * k + 16) & 31]) : "v"(y[(2 * k + 5) & 31]), "v"(y[(2 * k + 7) & 31]));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x[(2 * k + 17) & 31]) : "v"(y[(2 * k + 6) & 31]), "v"(y[(2 * k + 8) & 31]));
+                } else {
+#pragma unroll
+                    for (int f = 0; f < 4; ++f)
+                        asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(y[(4 * k + f) & 31]) : "v"(x[(4 * k + f) & 31]), "v"(x[(4 * k + f + 1) & 31]));
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int k = 0; k < 8; ++k) fold ^= vb[k][2] ^ vt[2 * k][1] ^ vt[2 * k + 1][0];
+        } else if constexpr (MODE >= 11) {
+            // 16 MFMAs, each followed by independent VALU work of the same
+            // wave: 4 fmas (11), 2 exps + 2 fmas (12), 8 fmas (13)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[k & 3]) : "v"(a), "v"(b));
+                if constexpr (MODE == 12) {
+                    asm volatile("v_exp_f32 %0, %1" : "=v"(y[(2 * k) & 31]) : "v"(x[(2 * k) & 31]));
+                    asm volatile("v_exp_f32 %0, %1" : "=v"(y[(2 * k + 1) & 31]) : "v"(x[(2 * k + 1) & 31]));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x[(2 * k + 16) & 31]) : "v"(y[(2 * k + 5) & 31]), "v"(y[(2 * k + 7) & 31]));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x[(2 * k + 17) & 31]) : "v"(y[(2 * k + 6) & 31]), "v"(y[(2 * k + 8) & 31]));
+                } else {
+#pragma unroll
+                    for (int f = 0; f < (MODE == 11 ? 4 : 8); ++f) {
+                        const int i = (MODE == 11 ? 4 : 8) * k + f;
+                        asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(y[i & 31]) : "v"(x[i & 31]), "v"(x[(i + 1) & 31]));
+                    }
+                }
+            }
         } else {
             // 8: group A (waves 0-3) 16 MFMAs, group B (waves 4-7, one on
             // each SIMD beside an A wave) 32 exps + 32 fmas; 9: A alone;
@@ -241,9 +288,9 @@ extern "C" int pkv_probe_stream_read(const void *buf, size_t bytes, int32_t mode
 
 extern "C" int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blocks, uint64_t *cycles,
                                int32_t *sink, void *stream) {
-    if (!cycles || !sink || blocks <= 0 || mode < 0 || mode > 10) return 1;
+    if (!cycles || !sink || blocks <= 0 || mode < 0 || mode > 15) return 1;
     if (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4) return 1;
-    if (mode >= 8 && waves_per_simd != 2) return 1;
+    if (mode >= 8 && mode <= 10 && waves_per_simd != 2) return 1;
     const int32_t waves = 4 * waves_per_simd;
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipErrorInvalidValue;
@@ -259,6 +306,11 @@ extern "C" int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blo
         case 8: e = launch_issue<8>(blocks, waves, cycles, sink, s); break;
         case 9: e = launch_issue<9>(blocks, waves, cycles, sink, s); break;
         case 10: e = launch_issue<10>(blocks, waves, cycles, sink, s); break;
+        case 11: e = launch_issue<11>(blocks, waves, cycles, sink, s); break;
+        case 12: e = launch_issue<12>(blocks, waves, cycles, sink, s); break;
+        case 13: e = launch_issue<13>(blocks, waves, cycles, sink, s); break;
+        case 14: e = launch_issue<14>(blocks, waves, cycles, sink, s); break;
+        case 15: e = launch_issue<15>(blocks, waves, cycles, sink, s); break;
     }
     return e == hipSuccess ? 0 : 3;
 }
