@@ -555,7 +555,8 @@ ISSUE_MODES = {   # mode: (what one pass issues, instructions the rate is per)
     11: ("16 x (MFMA + 4 fma, one wave), per MFMA", 16), 12: ("16 x (MFMA + 2 exp + 2 fma, one wave), per MFMA", 16),
     13: ("16 x (MFMA + 8 fma, one wave), per MFMA", 16),
     14: ("16 x (MFMA + 1.5 reads + 4 fma, one wave), per MFMA", 16),
-    15: ("16 x (MFMA + 1.5 reads + 2 exp + 2 fma, one wave), per MFMA", 16)}
+    15: ("16 x (MFMA + 1.5 reads + 2 exp + 2 fma, one wave), per MFMA", 16),
+    16: ("mode 14 with AGPR accumulators, per MFMA", 16), 17: ("mode 15 with AGPR accumulators, per MFMA", 16)}
 
 
 def issue_rates() -> str:
@@ -586,8 +587,8 @@ def issue_rates() -> str:
 
     out = ["| Block | waves per SIMD | cycles per instruction per SIMD | per wave |", "|---|---|---|---|"]
     for mode, (name, n) in ISSUE_MODES.items():
-        # (at 4 waves per SIMD modes 5, 6 and 11-15 exceed their 128 registers and spill)
-        for wps in ((1, 2) if mode in (5, 6, 11, 12, 13, 14, 15) else (1, 2, 4)):
+        # (at 4 waves per SIMD modes 5, 6 and 11-17 exceed their 128 registers and spill)
+        for wps in ((1, 2) if mode in (5, 6, 11, 12, 13, 14, 15, 16, 17) else (1, 2, 4)):
             c = run(mode, wps)[:, :4 * wps]
             per_simd = c.max(axis=1).mean() / (passes * n * wps)
             out.append(f"| {name} | {wps} | {per_simd:.1f} | {c.mean() / (passes * n):.1f} |")

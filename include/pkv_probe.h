@@ -54,7 +54,8 @@ int pkv_probe_stream_read(const void *buf, size_t bytes, int32_t mode, int32_t r
  *           8 v_fma_f32)
  *   mode 14 the tile mix of one wave: 16 MFMAs, 24 operand reads (as mode
  *           7) and 4 v_fma_f32 per MFMA; mode 15: the same with 2 v_exp_f32
- *           + 2 v_fma_f32 per MFMA
+ *           + 2 v_fma_f32 per MFMA; modes 16 and 17: modes 14 and 15 with
+ *           the accumulators in AGPRs
  * waves_per_simd is 1, 2 or 4. Returns 0, 1 for bad arguments, 3 when the
  * launch fails. Asynchronous on `stream`. */
 int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blocks, uint64_t *cycles,

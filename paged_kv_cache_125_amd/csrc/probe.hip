@@ -182,19 +182,23 @@ __global__ __launch_bounds__(NT) void issue_probe(uint64_t *cycles, int32_t *sin
             }
         } else if constexpr (MODE >= 14) {
             // the whole tile mix in one wave: 16 MFMAs with 24 operand
-            // reads (as mode 7) and 4 fmas (14) or 2 exps + 2 fmas (15) each
+            // reads (as mode 7) and 4 fmas (14, 16) or 2 exps + 2 fmas (15,
+            // 17) each; accumulators in VGPRs (14, 15) or AGPRs (16, 17)
             u32x4 vb[8];
             u32x2 vt[16];
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[k & 3]) : "v"(a), "v"(b));
+                if constexpr (MODE >= 16)
+                    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[k & 3]) : "v"(a), "v"(b));
+                else
+                    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[k & 3]) : "v"(a), "v"(b));
                 if (k & 1) {
                     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vt[k - 1]) : "v"(av[0][k & 3]), "i"((k >> 2) * 4096));
                     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vt[k]) : "v"(av[1][k & 3]), "i"((k >> 2) * 4096));
                 } else {
                     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(vb[k >> 1]) : "v"(ak[k >> 1]), "i"(0));
                 }
-                if constexpr (MODE == 15) {
+                if constexpr (MODE == 15 || MODE == 17) {
                     asm volatile("v_exp_f32 %0, %1" : "=v"(y[(2 * k) & 31]) : "v"(x[(2 * k) & 31]));
                     asm volatile("v_exp_f32 %0, %1" : "=v"(y[(2 * k + 1) & 31]) : "v"(x[(2 * k + 1) & 31]));
                     asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x[(2 * k + 16) & 31]) : "v"(y[(2 * k + 5) & 31]), "v"(y[(2 * k + 7) & 31]));
@@ -288,7 +292,7 @@ extern "C" int pkv_probe_stream_read(const void *buf, size_t bytes, int32_t mode
 
 extern "C" int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blocks, uint64_t *cycles,
                                int32_t *sink, void *stream) {
-    if (!cycles || !sink || blocks <= 0 || mode < 0 || mode > 15) return 1;
+    if (!cycles || !sink || blocks <= 0 || mode < 0 || mode > 17) return 1;
     if (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4) return 1;
     if (mode >= 8 && mode <= 10 && waves_per_simd != 2) return 1;
     const int32_t waves = 4 * waves_per_simd;
@@ -311,6 +315,8 @@ extern "C" int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blo
         case 13: e = launch_issue<13>(blocks, waves, cycles, sink, s); break;
         case 14: e = launch_issue<14>(blocks, waves, cycles, sink, s); break;
         case 15: e = launch_issue<15>(blocks, waves, cycles, sink, s); break;
+        case 16: e = launch_issue<16>(blocks, waves, cycles, sink, s); break;
+        case 17: e = launch_issue<17>(blocks, waves, cycles, sink, s); break;
     }
     return e == hipSuccess ? 0 : 3;
 }
