@@ -34,6 +34,34 @@ def test_probe_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_probe_library_rejects_bad_arguments_before_any_launch():
+    # the argument checks in pkv_probe_issue / pkv_probe_stream_read return 1
+    # before touching the device, so they run here without a GPU
+    from paged_kv_cache_125_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pkv_probe_issue.restype = ctypes.c_int
+    lib.pkv_probe_issue.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.pkv_probe_stream_read.restype = ctypes.c_int
+    lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    cyc = ctypes.c_void_p(0x1000)    # never dereferenced: every call below fails its checks first
+    sink = ctypes.c_void_p(0x2000)
+    for mode, wps, blocks in ((-1, 1, 1), (18, 1, 1), (0, 3, 1), (0, 1, 0), (8, 1, 1), (9, 4, 1), (10, 1, 1)):
+        assert lib.pkv_probe_issue(mode, wps, blocks, cyc, sink, None) == 1, (mode, wps, blocks)
+    assert lib.pkv_probe_issue(0, 1, 1, None, sink, None) == 1
+    assert lib.pkv_probe_issue(0, 1, 1, cyc, None, None) == 1
+    buf = ctypes.c_void_p(0x10000)
+    assert lib.pkv_probe_stream_read(None, 4096, 0, 0, 1, sink, None) == 1
+    assert lib.pkv_probe_stream_read(buf, 0, 0, 0, 1, sink, None) == 1
+    assert lib.pkv_probe_stream_read(buf, 4100, 0, 0, 1, sink, None) == 1      # not a multiple of 16
+    assert lib.pkv_probe_stream_read(ctypes.c_void_p(0x10008), 4096, 0, 0, 1, sink, None) == 1   # misaligned
+    assert lib.pkv_probe_stream_read(buf, 4096, 0, 0, 0, sink, None) == 1      # no blocks
+    assert lib.pkv_probe_stream_read(buf, 4096, 1, 300, 1, sink, None) == 1    # rows not 256-byte multiples
+    assert lib.pkv_probe_stream_read(buf, 4096, 1, 8192, 1, sink, None) == 1   # fewer bytes than one row
+    assert lib.pkv_probe_stream_read(buf, 4096, 2, 0, 1, sink, None) == 1      # unknown mode
+
+
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert len(names) >= 12
