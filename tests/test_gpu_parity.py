@@ -335,6 +335,37 @@ def test_mixed_batch(cuda, case):
     assert err <= 2e-2
 
 
+SHORT = [
+    # (num_q_heads, num_kv_heads, block_size): sequences of 1 to 33 query rows
+    # (all of a query block's live rows in its first wave, or one past it)
+    # across group sizes 1, 2, 3, 4 and 8; 0 = contiguous keys
+    (8, 8, 16), (16, 8, 256), (24, 8, 64), (32, 8, 16), (64, 8, 256), (16, 8, 0), (24, 8, 0),
+]
+
+
+@pytest.mark.parametrize("case", SHORT, ids=lambda c: f"g{c[0] // c[1]}-bs{c[2]}")
+def test_short_sequences(cuda, case):
+    hq, hkv, bs = case
+    if bs:
+        # query rows 1, 5, 31, 32, 33 and 1 against contexts of 1 to ~2.2k keys
+        lens = [1, 700, 2100, 64, 97, 2200]
+        lq = [1, 5, 31, 32, 33, 1]
+    else:
+        # fresh prompts (contiguous keys): Lk = Lq
+        lens = [1, 5, 31, 32, 33, 17]
+        lq = lens
+    cached = [n - q for n, q in zip(lens, lq)]
+    say(f"[gpu] short sequences Hq {hq} Hkv {hkv} bs {bs}: lens {lens} cached {cached}")
+    w = custom_workload(phase="prefill", seq_lens=lens, num_cached=cached, num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=128, block_size=bs or 16, seed=hq * 7 + bs)
+    out, kc, vc = gpu_run(to_device(w, "cuda"))
+    want, kp, vp, _ = oracle.run_workload(w)
+    assert np.array_equal(raw(kc), raw(kp)) and np.array_equal(raw(vc), raw(vp))
+    err = max_abs_err(out, want)
+    say(f"  max |err| = {err:.3e}")
+    assert err <= 2e-2
+
+
 def test_decode_in_varlen_matches_decode_kernel(cuda):
     say("[gpu] preset 6 (preset 2's batch as Lq = 1 varlen rows) vs the decode kernel")
     w = make_workload(6)
