@@ -316,8 +316,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // One key tile: start the direct loads of the next tile into `nxt`, then
     // compute on `cur`. The two buffers are distinct objects (restrict), which
     // lets the compiler read `cur` without waiting for the loads into `nxt`.
-    auto tile_step = [&](auto masked, const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
+    // `nmt`: key halves of the tile the wave computes: 2, or 1 (the lower
+    // half) on a diagonal tile whose upper half lies wholly above the wave's
+    // last row.
+    auto tile_step = [&](auto nmt, auto masked, const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt,
                          int k0, bool more) {
+        constexpr int NMT = decltype(nmt)::value;
         load_tile(k0 + kPfBN, nxt);
         const uint8_t *Ks = cur;
         const uint8_t *Vs = cur + kTileBytes;
@@ -328,7 +332,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) st[rb][mt][r] = 0.f;
             // The two key halves' chains alternate, and the K operand reads
@@ -338,7 +342,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
+                for (int mt = 0; mt < NMT; ++mt) {
                     const bf16x8 kab = __builtin_bit_cast(bf16x8,
                         *reinterpret_cast<const u32x4 *>(Ks + 32 * 256 * mt + koff[kk]));
 #pragma unroll
@@ -346,10 +350,10 @@ void prefill_mfma_kernel(PrefillArgs a) {
                         st[rb][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kab, qb[rb][kk], st[rb][mt], 0, 0, 0);
                 }
             if constexpr (RB == 1) {
-                constexpr int kLook = 6;
+                constexpr int kLook = NMT == 2 ? 6 : 4;
                 __builtin_amdgcn_sched_group_barrier(0x100, kLook, 0);   // the first K reads
 #pragma unroll
-                for (int i = 0; i < 16 - kLook; ++i) {
+                for (int i = 0; i < 8 * NMT - kLook; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the next read
                 }
@@ -365,7 +369,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 if constexpr (decltype(masked)::value) {
                     const int lim = my_pos[rb] - k0 - 4 * j;
 #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
+                    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
                             st[rb][mt][r] = (32 * mt + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : st[rb][mt][r];
@@ -375,14 +379,15 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 // unlike fmaxf, needs no quieting of its inputs first.
                 float xq[4];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
+                for (int g = 0; g < 2 * NMT; ++g) {
                     const int mt = g >> 1, r0 = 8 * (g & 1);
                     xq[g] = fmax3(st[rb][mt][r0], st[rb][mt][r0 + 1], st[rb][mt][r0 + 2]);
                     xq[g] = fmax3(xq[g], st[rb][mt][r0 + 3], st[rb][mt][r0 + 4]);
                     xq[g] = fmax3(xq[g], st[rb][mt][r0 + 5], st[rb][mt][r0 + 6]);
                     xq[g] = fmax3(xq[g], st[rb][mt][r0 + 7], xq[g]);
                 }
-                const float x4 = fmax3(fmax3(xq[0], xq[1], xq[2]), xq[3], xq[3]);
+                const float x4 = NMT == 2 ? fmax3(fmax3(xq[0], xq[1], xq[2]), xq[3], xq[3])
+                                          : __builtin_elementwise_maximum(xq[0], xq[1]);
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x4), __float_as_uint(x4), false, false);
                 mx[rb] = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
@@ -410,7 +415,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 const float mc = m[rb] * c;
                 float ls[4] = {0.f, 0.f, 0.f, 0.f};   // four short sum chains
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
+                for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
                     for (int ap = 0; ap < 2; ++ap) {
 #pragma unroll
@@ -421,12 +426,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
                             ls[2 * mt + ap] = __builtin_amdgcn_fdot2_f32_bf16(
                                 bf16x2{pb[rb][mt][ap][e], pb[rb][mt][ap][e + 1]}, ones, ls[2 * mt + ap], false);
                     }
-                l[rb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+                l[rb] += NMT == 2 ? (ls[0] + ls[1]) + (ls[2] + ls[3]) : ls[0] + ls[1];
             }
             // O^T += V^T P^T over 4 steps of 16 keys; each V^T operand (two
             // transpose reads of 4 consecutive key rows) feeds both row blocks.
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
                 for (int ap = 0; ap < 2; ++ap) {
                     const uint8_t *vrow = Vs + (32 * mt + 16 * ap) * 256;
@@ -469,22 +474,25 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // must have landed before the barrier hands its buffer to the other waves.
     int kt = 0;
     for (; kt + 1 < n_full; kt += 2) {
-        tile_step(std::false_type{}, lds[0], lds[1], kt * kPfBN, true);
+        tile_step(std::integral_constant<int, 2>{}, std::false_type{}, lds[0], lds[1], kt * kPfBN, true);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        tile_step(std::false_type{}, lds[1], lds[0], (kt + 1) * kPfBN, kt + 2 < n_kt);
+        tile_step(std::integral_constant<int, 2>{}, std::false_type{}, lds[1], lds[0], (kt + 1) * kPfBN, kt + 2 < n_kt);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     if (kt < n_full) {   // kt is even here
-        tile_step(std::false_type{}, lds[0], lds[1], kt * kPfBN, kt + 1 < n_kt);
+        tile_step(std::integral_constant<int, 2>{}, std::false_type{}, lds[0], lds[1], kt * kPfBN, kt + 1 < n_kt);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         ++kt;
     }
     for (; kt < n_kt; ++kt) {
         const int buf = kt & 1;
-        tile_step(std::true_type{}, lds[buf], lds[buf ^ 1], kt * kPfBN, kt + 1 < n_kt);
+        if (kt * kPfBN + 32 > pos_last)   // the upper key half is masked for every row of the wave
+            tile_step(std::integral_constant<int, 1>{}, std::true_type{}, lds[buf], lds[buf ^ 1], kt * kPfBN, kt + 1 < n_kt);
+        else
+            tile_step(std::integral_constant<int, 2>{}, std::true_type{}, lds[buf], lds[buf ^ 1], kt * kPfBN, kt + 1 < n_kt);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
