@@ -161,16 +161,18 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _used_on(stream, *tensors: Optional[torch.Tensor]) -> None:
-    """Device tensors the binding allocated itself (on the current stream)
-    and handed to kernels queued on another ``stream``: tell torch's caching
-    allocator, so that their memory is not given out again before that
-    stream's work has run."""
+def _alloc_on(stream, *shape, **kw) -> torch.Tensor:
+    """A device tensor the binding allocates itself for work it queues on
+    ``stream``: allocated in that stream's context, so that torch's caching
+    allocator orders any later reuse of its memory after that stream's work.
+    Allocated on the current stream instead (and only marked with
+    record_stream), it could receive a block that work still queued on the
+    current stream reads -- a block freed there is handed out again at once
+    -- and the upload or kernel on ``stream`` would overwrite it first."""
     if stream is None or stream == torch.cuda.current_stream():
-        return
-    for t in tensors:
-        if t is not None:
-            t.record_stream(stream)
+        return torch.empty(*shape, **kw)
+    with torch.cuda.stream(stream):
+        return torch.empty(*shape, **kw)
 
 
 def _token_stride(t: torch.Tensor) -> int:
@@ -444,9 +446,8 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
     if workspace is not None:
         _need(workspace.dtype == torch.uint8 and workspace.is_contiguous()
               and workspace.device == q.device, "workspace must be a contiguous uint8 tensor on q's device")
-    own_out = out is None
-    if own_out:
-        out = torch.empty((total_q, hq, d), dtype=q.dtype, device=q.device)
+    if out is None:
+        out = _alloc_on(stream, (total_q, hq, d), dtype=q.dtype, device=q.device)
     _need(workspace is None or workspace.numel() >= prefill_workspace_bytes(),
           "workspace is smaller than prefill_workspace_bytes()")
     _check(lib().pkv_prefill_attention_varlen(
@@ -454,8 +455,6 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
         _ptr(block_tables), maxb, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, total_q,
         int(max_seqlen_q), int(max_seqlen_k), nb, bs, hq, hkv, d, float(scale), _dtype_code(q),
         _ptr(out), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
-    if own_out:
-        _used_on(stream, out)
     return out
 
 
@@ -499,19 +498,17 @@ def decode_attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
               "workspace must be a contiguous uint8 tensor")
     _one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
              context_lens=context_lens, out=out, workspace=workspace)
-    own_out, own_ws = out is None, workspace is None
-    if own_out:
-        out = torch.empty((B, hq, d), dtype=q.dtype, device=q.device)
+    if out is None:
+        out = _alloc_on(stream, (B, hq, d), dtype=q.dtype, device=q.device)
     need = decode_workspace_bytes(B, max_context_len, hq, hkv, d, bs, q.dtype, partition_size)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _alloc_on(stream, need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_decode_attention_paged(
         _ptr(q), _token_stride(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), B, int(max_context_len), nb, bs, hq, hkv, d,
         float(scale), _dtype_code(q), _ptr(out), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream)))
-    _used_on(stream, out if own_out else None, workspace if own_ws else None)
     return out
 
 
@@ -636,9 +633,8 @@ def _pack(prefill: bool, seq_lens, num_cached, block_tables, block_size: int, de
     if device is None or torch.device(device).type == "cpu":
         dev = host
     else:
-        own_dev = dev_buffer is None
-        if own_dev:
-            dev = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if dev_buffer is None:
+            dev = _alloc_on(stream, nbytes, dtype=torch.uint8, device=device)
         else:
             if dev_buffer.dtype != torch.uint8 or dev_buffer.device.type != "cuda" \
                     or not dev_buffer.is_contiguous() or dev_buffer.numel() < nbytes:
@@ -647,8 +643,6 @@ def _pack(prefill: bool, seq_lens, num_cached, block_tables, block_size: int, de
         _check(L.pkv_upload(P(host.data_ptr()), P(dev.data_ptr()), nbytes, _stream(stream)))
         if host_buffer is None:
             _hold_until_uploaded(host, stream)
-        if own_dev:
-            _used_on(stream, dev)
     res = _views(layout, dev)
     res["host_buffer"] = host
     res["layout"] = layout

@@ -97,12 +97,19 @@ def decode_rows_first(s: StepInputs) -> int:
 
 def run_mixed_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                    k_cache: torch.Tensor, v_cache: torch.Tensor, out: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   side_stream=None) -> torch.Tensor:
     """A mixed (chunked-prefill) step whose decode rows come first: those go
     through the decode kernel -- the K/V of a kv head streamed once for its
     whole query-head group and split over every SIMD -- and the prompts and
     prompt chunks that follow through the varlen call. Same results as
-    ``run_step`` on the whole batch."""
+    ``run_step`` on the whole batch.
+
+    With ``side_stream`` (a default-priority stream) the prompt part runs
+    there, ordered after the work already queued on ``stream``, and
+    ``stream`` waits for it before returning: the two parts write disjoint
+    rows and cache slots, so the chunks can start on CUs whose decode waves
+    have finished."""
     nd = decode_rows_first(s)
     if nd == 0 or nd == len(s.seq_lens):
         return run_step(s if nd == 0 else StepInputs("decode", s.seq_lens, s.num_cached,
@@ -114,9 +121,15 @@ def run_mixed_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: t
                      s.block_size, s.scale)
     pre = StepInputs("prefill", s.seq_lens[nd:], s.num_cached[nd:], s.block_tables[nd:],
                      s.block_size, s.scale, s.use_block_tables)
+    main = stream if stream is not None else torch.cuda.current_stream()
+    if side_stream is not None:
+        side_stream.wait_stream(main)
     run_step(dec, q[:nd], k_new[:nd], v_new[:nd], k_cache, v_cache, out=out[:nd],
-             workspace=workspace, stream=stream)
-    run_step(pre, q[nd:], k_new[nd:], v_new[nd:], k_cache, v_cache, out=out[nd:], stream=stream)
+             workspace=workspace, stream=main)
+    run_step(pre, q[nd:], k_new[nd:], v_new[nd:], k_cache, v_cache, out=out[nd:],
+             stream=side_stream if side_stream is not None else main)
+    if side_stream is not None:
+        main.wait_stream(side_stream)
     return out
 
 

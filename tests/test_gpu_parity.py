@@ -424,7 +424,11 @@ def test_mixed_step_split_matches_one_varlen_call(cuda):
     write_ranges(w.hist, w.block_tables, w.block_size, wd.k_hist, wd.v_hist, kc, vc)
     out = run_mixed_step(s, wd.q, wd.k_new, wd.v_new, kc, vc)
     one = run_step(s, wd.q, wd.k_new, wd.v_new, kc, vc)
+    # the same split with the prompt chunks on a second stream
+    side = torch.cuda.Stream()
+    two = run_mixed_step(s, wd.q, wd.k_new, wd.v_new, kc, vc, side_stream=side)
     torch.cuda.synchronize()
     want, *_ = oracle.run_workload(w)
     assert max_abs_err(out, want) <= 2e-2
     assert (out.float() - one.float()).abs().max().item() <= 2e-2
+    assert torch.equal(two, out)
