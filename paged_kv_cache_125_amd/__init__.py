@@ -10,6 +10,12 @@ Entry points (same names as the C functions, without the ``pkv_`` prefix):
 ``store_kvcache``, ``prefill_attention_varlen``, ``decode_attention_paged``,
 ``decode_attention_paged_noalloc``, ``decode_workspace_bytes``,
 ``decode_partition_size``, ``pack_prefill``, ``pack_decode``.
+
+Streams: every call queues its work on ``stream`` (torch's current stream
+when None). Device buffers the binding allocates itself for that work
+(packed metadata, an output or workspace not given by the caller) are
+allocated in that stream's context, and pinned staging buffers are held until
+their upload has run; buffers the caller passes stay the caller's to order.
 """
 from __future__ import annotations
 
