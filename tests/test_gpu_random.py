@@ -17,7 +17,7 @@ from workloads import custom_workload
 pytestmark = pytest.mark.gpu
 
 TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
-N_CASES = 24
+N_CASES = 48
 
 
 def _shape(rng):
