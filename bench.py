@@ -68,6 +68,8 @@ WORKLOADS = {
     "mixed": [("prefill", 7), ("prefill+split", 7)],
     # preset 3's step with the rotary embedding fused into the store
     "rope-store": [("prefill+rope", 3)],
+    # preset 3's store and attention as two calls, then as one fused call
+    "fused-store": [("prefill", 3), ("prefill+fused", 3)],
     # preset 2's decode, plus 28-layer decode steps eager vs replayed hipGraphs
     "decode-graph": [("decode", 2)],
 }
@@ -153,9 +155,12 @@ class Part:
         self.pkv = pkv
         # "prefill+rope": the store is the fused rotary embedding + store;
         # "prefill+split": a mixed step's decode rows (first) go through the
-        # decode kernel, the rest through the varlen call
+        # decode kernel, the rest through the varlen call;
         self.rope = phase.endswith("+rope")
         self.split = phase.endswith("+split")
+        # "prefill+fused": store and attention in one call
+        # (prefill_store_attention_varlen); the store interval is then empty
+        self.fused = phase.endswith("+fused")
         phase = phase.split("+")[0]
         self.phase, self.preset = phase, preset
         self.copies = []
@@ -256,6 +261,13 @@ class Part:
             meta = pkv.pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size,
                                     host_buffer=hb, dev_buffer=db)
             rec(1)
+            if self.fused:
+                rec(2)
+                pkv.prefill_store_attention_varlen(w.q, w.k_new, w.v_new, kc, vc, meta["slot_mapping"],
+                                                   meta["cu_seqlens_q"], meta["max_seqlen_q"], s.scale,
+                                                   out=out)
+                rec(3)
+                return meta
             if self.rope:
                 pkv.rope_store_kvcache(w.q, w.k_new, w.v_new, kc, vc, meta["slot_mapping"],
                                        meta["positions"], self.cos_sin,
@@ -286,15 +298,23 @@ class Part:
         t_store = float(np.mean(self.times["store"]))
         t_pack = float(np.mean(self.times["pack"]))
         sb = rope_store_bytes(w) if self.rope else store_bytes(w)
-        d = {"workload": w.name + ("+rope" if self.rope else "") + ("+split" if self.split else ""),
-             "preset": self.preset,
-             "phase": self.phase, "store": "rope_store_kvcache" if self.rope else "store_kvcache",
+        d = {"workload": w.name + ("+rope" if self.rope else "") + ("+split" if self.split else "")
+             + ("+fused" if self.fused else ""),
+             "preset": self.preset, "phase": self.phase,
+             "store": ("rope_store_kvcache" if self.rope else
+                       "in the attention call (prefill_store_attention_varlen)" if self.fused else
+                       "store_kvcache"),
              "num_seqs": len(w.seq_lens), "tokens_q": w.total_q,
              "context_tokens": int(sum(w.seq_lens)),
              "pack_us": t_pack * 1e6, "store_us": t_store * 1e6, "attention_us": t_attn * 1e6,
              "attention_us_p10": float(np.percentile(self.times["attention"], 10)) * 1e6,
              "attention_us_p90": float(np.percentile(self.times["attention"], 90)) * 1e6,
-             "store_GBps": sb / t_store / 1e9, "store_frac_hbm": sb / t_store / 1e9 / HBM_PEAK_GBS}
+             "store_GBps": None, "store_frac_hbm": None}
+        if self.fused:
+            # one interval holds both: its rate counts the attention's work only
+            d.update({"store_us": 0.0, "store_and_attention_us": t_attn * 1e6})
+        else:
+            d.update({"store_GBps": sb / t_store / 1e9, "store_frac_hbm": sb / t_store / 1e9 / HBM_PEAK_GBS})
         if self.phase == "decode":
             b = decode_bytes(w)
             d.update({"attention_bytes": b, "attention_GBps": b / t_attn / 1e9,
@@ -653,7 +673,8 @@ def size_matched_rates(parts, summaries, per_cu: int, cycles: int, reps: int = 2
         dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(n)]
         t = timed(lambda i: dsts[i % n].copy_(srcs[i % n]))
         rec["device_copy"] = {"bytes": 2 * half, "us": t * 1e6, "GBps": 2 * half / t / 1e9,
-                              "store_over_copy": sm["store_GBps"] / (2 * half / t / 1e9)}
+                              "store_over_copy": (None if sm["store_GBps"] is None else
+                                                  sm["store_GBps"] / (2 * half / t / 1e9))}
         del srcs, dsts
         torch.cuda.empty_cache()
         out[sm["workload"]] = rec
@@ -1075,7 +1096,7 @@ def main():
         sec["decode_frac_of_hbm_peak"] = dec["attention_frac_hbm"]
     # every part's attention figure, by workload
     for sm in summaries:
-        k = names[sm["preset"]]
+        k = names[sm["preset"]] + ("+fused-store" if sm["workload"].endswith("+fused") else "")
         if sm["phase"] == "decode":
             sec.setdefault("per_workload", {})[k] = {
                 "GBps": sm["attention_GBps"], "frac_of_hbm_peak": sm["attention_frac_hbm"],

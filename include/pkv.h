@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 
 typedef enum {
     PKV_OK = 0,
@@ -166,6 +166,48 @@ int pkv_prefill_attention_varlen(const void *q, int64_t q_token_stride, const vo
  * persistent grid's counters; the arguments are those of the call). */
 size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
+
+/* ---------------------------------------------------------------------------
+ * prefill_store_attention_varlen: store_kvcache and prefill_attention_varlen
+ * of a batch with no cached prefix, in one call ([MR] the attention layer's
+ * forward, which writes the step's K/V through slot_mapping and then runs
+ * varlen attention over them; "prepare_prefill" for the metadata).
+ *
+ * The result equals pkv_store_kvcache(k, v, kv_token_stride, kv_token_stride,
+ * k_cache, v_cache, slot_mapping, total_q, num_blocks, block_size, ...)
+ * followed on the same stream by pkv_prefill_attention_varlen with
+ * block_tables == NULL and cu_seqlens_q == cu_seqlens_k == cu_seqlens: the
+ * keys of sequence s are its own rows [cu_seqlens[s], cu_seqlens[s+1]) of k/v
+ * (Lk_s == Lq_s), and row i of k/v is also written to cache slot
+ * slot_mapping[i] (skipped when negative or past the pool).
+ *
+ * For bf16 and head_dim 128 this is one launch: after its attention, the
+ * workgroup of each query block that serves the first query head of a kv head
+ * copies that block's K/V rows into their slots (the rows were loaded for the
+ * block's last key tiles moments before). Other dtypes and head sizes run the
+ * store kernel and then the attention kernel. Rows outside every sequence's
+ * range, and rows of a sequence the attention skips (see above), may be left
+ * unstored; with cu_seqlens a prefix sum from 0 to total_q (what
+ * pkv_pack_prefill writes) every row is stored. The cache writes are not read
+ * by this call, so k/v and the caches may be any distinct buffers.
+ *
+ *  q, out          as in pkv_prefill_attention_varlen.
+ *  k, v            [total_q, num_kv_heads, head_dim], token stride
+ *                  kv_token_stride, q's dtype.
+ *  k_cache,v_cache [num_blocks, block_size, num_kv_heads, head_dim].
+ *  slot_mapping    device int32 [total_q]; slots unique within the call.
+ *  cu_seqlens      device int32 [num_seqs + 1]; max_seqlen bounds Lq_s.
+ * Errors as in the two calls it combines; the pool shape only sizes the slot
+ * range (num_blocks * block_size <= 2^31 - 1, block_size any positive value).
+ * Uses no workspace (always the one-workgroup-per-item grid). */
+int pkv_prefill_store_attention_varlen(const void *q, int64_t q_token_stride, const void *k,
+                                       const void *v, int64_t kv_token_stride, void *k_cache,
+                                       void *v_cache, const int32_t *slot_mapping,
+                                       int32_t num_blocks, int32_t block_size,
+                                       const int32_t *cu_seqlens, int32_t num_seqs,
+                                       int32_t total_q, int32_t max_seqlen, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, float scale,
+                                       int32_t dtype, void *out, void *stream);
 
 /* ---------------------------------------------------------------------------
  * decode_attention_paged  ([MR] "prepare_decode": one query per sequence,

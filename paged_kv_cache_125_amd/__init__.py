@@ -28,7 +28,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpkv.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 PKV_F32, PKV_BF16 = 0, 1
 _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_ELAUNCH", 4: "PKV_ENOSPACE"}
@@ -37,6 +37,7 @@ EXPORTED = [
     "pkv_abi_version", "pkv_last_error", "pkv_store_kvcache", "pkv_prefill_attention_varlen",
     "pkv_decode_attention_paged", "pkv_decode_partition_size", "pkv_decode_workspace_bytes",
     "pkv_decode_attention_paged_noalloc", "pkv_prefill_workspace_bytes",
+    "pkv_prefill_store_attention_varlen",
     "pkv_plan_prefill", "pkv_pack_prefill", "pkv_plan_decode", "pkv_pack_decode", "pkv_upload",
     "pkv_rope_cos_sin_table", "pkv_rope_store_kvcache",
     "pkv_xxh64", "pkv_block_hash", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
@@ -84,6 +85,9 @@ def lib():
     L.pkv_prefill_attention_varlen.restype = ctypes.c_int
     L.pkv_prefill_attention_varlen.argtypes = [P, i64, P, P, i64, P, P, P, i32, P, P, i32, i32, i32,
                                                i32, i32, i32, i32, i32, i32, f32, i32, P, P, sz, P]
+    L.pkv_prefill_store_attention_varlen.restype = ctypes.c_int
+    L.pkv_prefill_store_attention_varlen.argtypes = [P, i64, P, P, i64, P, P, P, i32, i32, P, i32, i32,
+                                                     i32, i32, i32, i32, f32, i32, P, P]
     L.pkv_prefill_workspace_bytes.restype = sz
     L.pkv_prefill_workspace_bytes.argtypes = [i32] * 6
     L.pkv_decode_attention_paged.restype = ctypes.c_int
@@ -461,6 +465,44 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
         _ptr(block_tables), maxb, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, total_q,
         int(max_seqlen_q), int(max_seqlen_k), nb, bs, hq, hkv, d, float(scale), _dtype_code(q),
         _ptr(out), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out
+
+
+def prefill_store_attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                   k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   slot_mapping: torch.Tensor, cu_seqlens: torch.Tensor,
+                                   max_seqlen: int, scale: float, *,
+                                   out: Optional[torch.Tensor] = None,
+                                   stream=None) -> torch.Tensor:
+    """pkv_prefill_store_attention_varlen: store_kvcache(k, v, k_cache, v_cache,
+    slot_mapping) and prefill_attention_varlen over the call's own k/v rows
+    (no cached prefix; cu_seqlens serves as both cu_seqlens_q and _k), in one
+    launch on the bf16 head_dim-128 path."""
+    _need(q.dim() == 3, "q must be [tokens, num_q_heads, head_dim]")
+    _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
+    total_q, hq, d = q.shape
+    _rows(q, "q", hq, d, q.dtype, 0)
+    _pool(k_cache, v_cache, q.dtype)
+    nb, bs, hkv, _ = k_cache.shape
+    _need(k_cache.shape[3] == d, "cache head_dim differs from q's")
+    _rows(k, "k", hkv, d, q.dtype, total_q)
+    _rows(v, "v", hkv, d, q.dtype, total_q)
+    kv_stride = _token_stride(k)
+    if _token_stride(v) != kv_stride:
+        raise ValueError("k and v must share a token stride")
+    _int32_vec(slot_mapping, "slot_mapping", total_q)
+    _int32_vec(cu_seqlens, "cu_seqlens", 1)
+    num_seqs = int(cu_seqlens.numel()) - 1
+    if out is not None:
+        _out(out, q)
+    _one_gpu(q=q, k=k, v=v, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping,
+             cu_seqlens=cu_seqlens, out=out)
+    if out is None:
+        out = _alloc_on(stream, (total_q, hq, d), dtype=q.dtype, device=q.device)
+    _check(lib().pkv_prefill_store_attention_varlen(
+        _ptr(q), _token_stride(q), _ptr(k), _ptr(v), kv_stride, _ptr(k_cache), _ptr(v_cache),
+        _ptr(slot_mapping), nb, bs, _ptr(cu_seqlens), num_seqs, total_q, int(max_seqlen), hq, hkv,
+        d, float(scale), _dtype_code(q), _ptr(out), _stream(stream)))
     return out
 
 

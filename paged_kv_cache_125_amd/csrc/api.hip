@@ -192,15 +192,22 @@ static int check_pool(const char *fn, const void *kc, const void *vc, const int3
     return PKV_OK;
 }
 
-extern "C" int pkv_prefill_attention_varlen(
-    const void *q, int64_t q_token_stride, const void *k, const void *v, int64_t kv_token_stride,
-    const void *k_cache, const void *v_cache, const int32_t *block_tables,
+// The two prefill entry points; st is the fused store's destination (null
+// for plain attention).
+struct PrefillStore {
+    void *kc, *vc;
+    const int32_t *slots;
+    int32_t num_slots;
+};
+
+static int prefill_call(
+    const char *fn, const void *q, int64_t q_token_stride, const void *k, const void *v,
+    int64_t kv_token_stride, const void *k_cache, const void *v_cache, const int32_t *block_tables,
     int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
     int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
     int32_t num_blocks, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, float scale, int32_t dtype, void *out, void *workspace,
-    size_t workspace_bytes, void *stream) {
-    const char *fn = "pkv_prefill_attention_varlen";
+    size_t workspace_bytes, const PrefillStore *st, void *stream) {
     int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs, scale);
     if (rc) return rc;
     if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
@@ -260,6 +267,12 @@ extern "C" int pkv_prefill_attention_varlen(
     a.max_seqlen_q = max_seqlen_q;
     a.max_seqlen_k = max_seqlen_k;
     a.total_q = total_q;
+    if (st) {
+        a.store_kc = st->kc;
+        a.store_vc = st->vc;
+        a.slots = st->slots;
+        a.num_slots = st->num_slots;
+    }
     // Longest query blocks first across pairs when the batch's K/V fits in half
     // the 256 MB MALL: contiguous keys are the call's own rows, paged keys are
     // bounded by num_seqs * max_seqlen_k.
@@ -268,6 +281,46 @@ extern "C" int pkv_prefill_attention_varlen(
         a.by_rank = keys * num_kv_heads * head_dim * 2 * 2 <= (int64_t(128) << 20);
     }
     return launched(pkv::launch_prefill(a, dtype, (hipStream_t)stream), fn);
+}
+
+extern "C" int pkv_prefill_attention_varlen(
+    const void *q, int64_t q_token_stride, const void *k, const void *v, int64_t kv_token_stride,
+    const void *k_cache, const void *v_cache, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+    int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_blocks, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t dtype, void *out, void *workspace,
+    size_t workspace_bytes, void *stream) {
+    return prefill_call("pkv_prefill_attention_varlen", q, q_token_stride, k, v, kv_token_stride,
+                        k_cache, v_cache, block_tables, max_blocks_per_seq, cu_seqlens_q,
+                        cu_seqlens_k, num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_blocks,
+                        block_size, num_q_heads, num_kv_heads, head_dim, scale, dtype, out,
+                        workspace, workspace_bytes, nullptr, stream);
+}
+
+extern "C" int pkv_prefill_store_attention_varlen(
+    const void *q, int64_t q_token_stride, const void *k, const void *v, int64_t kv_token_stride,
+    void *k_cache, void *v_cache, const int32_t *slot_mapping, int32_t num_blocks,
+    int32_t block_size, const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_q,
+    int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+    int32_t dtype, void *out, void *stream) {
+    const char *fn = "pkv_prefill_store_attention_varlen";
+    if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
+    if (block_size <= 0 || num_blocks <= 0) return fail(PKV_EINVAL, "%s: non-positive pool shape", fn);
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    if (num_slots > INT32_MAX) return fail(PKV_EINVAL, "%s: pool has more than 2^31-1 slots", fn);
+    if (num_kv_heads > 0 && head_dim > 0 && ((int64_t)num_kv_heads * head_dim * elem_size(dtype)) % 16)
+        return fail(PKV_EUNSUPPORTED, "%s: row bytes not a multiple of 16", fn);
+    if (total_q > 0 && num_seqs > 0 && max_seqlen > 0) {
+        if (!k_cache || !v_cache || !slot_mapping) return fail(PKV_EINVAL, "%s: null cache or slot_mapping", fn);
+        if (!aligned16(k_cache) || !aligned16(v_cache))
+            return fail(PKV_EINVAL, "%s: caches must be 16-byte aligned", fn);
+    }
+    const PrefillStore st = {k_cache, v_cache, slot_mapping, (int32_t)num_slots};
+    return prefill_call(fn, q, q_token_stride, k, v, kv_token_stride, nullptr, nullptr, nullptr, 0,
+                        cu_seqlens, cu_seqlens, num_seqs, total_q, max_seqlen, max_seqlen,
+                        num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                        out, nullptr, 0, &st, stream);
 }
 
 extern "C" size_t pkv_prefill_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) {

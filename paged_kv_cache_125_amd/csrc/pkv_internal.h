@@ -89,6 +89,11 @@ struct PrefillArgs {
     int32_t total_q;           // rows of q and out; a sequence outside them is skipped
     int32_t by_rank;           // grid order: longest query blocks first across pairs (set by the host)
     uint32_t *work_ctr;        // persistent grid: 8 per-XCD claim counters + 1 exit counter, or null
+    // Fused store (contiguous keys only): k/v row i is also copied to row
+    // slots[i] of these caches ([num_slots, Hkv, d]) when 0 <= slots[i] < num_slots.
+    void *store_kc = nullptr, *store_vc = nullptr;
+    const int32_t *slots = nullptr;
+    int32_t num_slots = 0;
 };
 // Bytes of the prefill workspace (the persistent grid's counters).
 constexpr size_t kPrefillWorkspaceBytes = 256;

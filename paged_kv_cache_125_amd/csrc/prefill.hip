@@ -87,9 +87,13 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __attribute__
 
 // NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
 // owns BM = 32 * RB * NW rows of one query head. WPE waves share one SIMD.
-template <int SRC, int NW, int RB, int WPE, bool PERSIST>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void prefill_mfma_kernel(PrefillArgs a) {
+// STORE (contiguous keys only): the workgroups of the first query head of
+// each kv head also copy their query block's own K/V rows into the cache
+// (store_kvcache fused into the attention launch).
+template <int SRC, int NW, int RB, int WPE, bool PERSIST, bool STORE>
+__device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
+    static_assert(!STORE || (SRC == kContiguous && RB == 1 && !PERSIST),
+                  "the fused store is built for the fixed grid over contiguous keys");
     constexpr int BM = 32 * RB * NW;         // query rows per workgroup (one query head)
     constexpr int LPW = 16 / NW;   // 1 KiB direct-load instructions per wave per K (or V) tile
     static_assert(NW * LPW == 16 && NW >= 2, "waves must split a tile evenly");
@@ -192,6 +196,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
             if (row_ok[rb]) w = ld16(q + 16 * kk);
             qb[rb][kk] = __builtin_bit_cast(bf16x8, w);
         }
+    }
+    // Fused store: the cache slot of the wave's row r32 (key row == query row
+    // with contiguous keys), loaded with q; -1 for rows past the sequence.
+    int my_slot = -1;
+    if constexpr (STORE) {
+        if (row_ok[0]) my_slot = a.slots[k_start + q0 + 32 * wh + r32];
     }
     const int kend = min(Lk, off + min(q0 + BM, Lq));   // keys this block needs
     const int n_kt = (kend + kPfBN - 1) / kPfBN;
@@ -508,6 +518,31 @@ void prefill_mfma_kernel(PrefillArgs a) {
         // store writes four full rows instead of 32 scattered 16-byte pieces.
         constexpr int kPitch = 272;
         uint8_t *stg = &lds[0][0] + kPitch * 32 * wave;
+        const int rbase = q0 + 32 * wh;
+        // Fused store: the K/V rows of the wave's 32 query rows go to their
+        // cache slots, four whole 256-byte rows per instruction. The G query
+        // heads of a kv head share them out (instruction i falls to head
+        // i % G), and the loads go out before the output epilogue, so the
+        // round trip overlaps it; the last two tile steps read these rows,
+        // so this XCD's L2 serves them. Rows past the sequence and slots
+        // outside the pool are skipped, as in store_kvcache.
+        u32x4 kw[8], vw[8];
+        int slot[8];
+        if constexpr (STORE) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int rr = 4 * i + (lane >> 4), chunk = lane & 15;
+                slot[i] = -1;
+                if (i % HG == hg) {   // wave-uniform
+                    slot[i] = __shfl(my_slot, rr);
+                    if ((uint32_t)slot[i] < (uint32_t)a.num_slots) {
+                        const int64_t src = (int64_t)(k_start + rbase + rr) * a.kv_stride + kvh * kPfD + 8 * chunk;
+                        kw[i] = ld16((const uint16_t *)a.k + src);
+                        vw[i] = ld16((const uint16_t *)a.v + src);
+                    }
+                }
+            }
+        }
         const float lt = xor32_sum(l[0]);
         const float inv = row_ok[0] ? 1.f / lt : 0.f;
         // o[0][nt][4*g + c] = O[row][d = 32*nt + 8*g + 4*j + c]
@@ -520,7 +555,6 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 w[1] = pack_bf16x2(o[0][nt][4 * g + 2] * inv, o[0][nt][4 * g + 3] * inv);
                 *reinterpret_cast<u32x2 *>(stg + r32 * kPitch + 2 * (32 * nt + 8 * g + 4 * j)) = w;
             }
-        const int rbase = q0 + 32 * wh;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int rr = 4 * i + (lane >> 4), chunk = lane & 15;
@@ -528,6 +562,17 @@ void prefill_mfma_kernel(PrefillArgs a) {
             if (rbase + rr < Lq) {
                 uint16_t *out = (uint16_t *)a.out + ((int64_t)(q_start + rbase + rr) * a.Hq + h) * kPfD;
                 *reinterpret_cast<u32x4 *>(out + 8 * chunk) = v;
+            }
+        }
+        if constexpr (STORE) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int chunk = lane & 15;
+                if ((uint32_t)slot[i] < (uint32_t)a.num_slots) {
+                    const int64_t dst = ((int64_t)slot[i] * a.Hkv + kvh) * kPfD + 8 * chunk;
+                    *reinterpret_cast<u32x4 *>((uint16_t *)a.store_kc + dst) = kw[i];
+                    *reinterpret_cast<u32x4 *>((uint16_t *)a.store_vc + dst) = vw[i];
+                }
             }
         }
     } else {
@@ -700,6 +745,19 @@ void prefill_mfma_kernel(PrefillArgs a) {
     }
 }
 
+template <int SRC, int NW, int RB, int WPE, bool PERSIST>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void prefill_mfma_kernel(PrefillArgs a) {
+    prefill_mfma_body<SRC, NW, RB, WPE, PERSIST, false>(a);
+}
+
+// Contiguous keys with the call's K/V rows also stored into the cache.
+template <int NW, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void prefill_store_mfma_kernel(PrefillArgs a) {
+    prefill_mfma_body<kContiguous, NW, 1, WPE, false, true>(a);
+}
+
 template <typename T>
 __device__ __forceinline__ float pf_load(const T *p, int64_t i);
 template <>
@@ -804,9 +862,9 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
         // the caller gave a workspace and the item tables fit in LDS.
         const bool persist = a.work_ctr != nullptr && (pairs + 7) / 8 <= kPfMaxXcdPairs &&
                              qblocks <= kPfMaxQblocks;
-        int64_t nwg = 8 * ((pairs + 7) / 8) * qblocks * a.group;
-        if (persist) nwg = 8 * ((2 * prefill_cus() + 7) / 8);
-        if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+        const int64_t nwg_fixed = 8 * ((pairs + 7) / 8) * qblocks * a.group;
+        if (nwg_fixed > 0x7fffffff) return hipErrorInvalidValue;
+        const int64_t nwg = persist ? 8 * ((2 * prefill_cus() + 7) / 8) : nwg_fixed;
         const dim3 grid((unsigned)nwg), block(64 * NW);
 #define PKV_MFMA_LAUNCH(P)                                                                                \
     do {                                                                                                  \
@@ -817,10 +875,33 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
         else                                                                                              \
             hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2, P>), grid, block, 0, stream, a);  \
     } while (0)
-        if (persist) PKV_MFMA_LAUNCH(true);
-        else PKV_MFMA_LAUNCH(false);
+        if (a.slots) {
+            if (a.paged) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((prefill_store_mfma_kernel<NW, 2>), dim3((unsigned)nwg_fixed), block, 0, stream, a);
+        } else if (persist) {
+            PKV_MFMA_LAUNCH(true);
+        } else {
+            PKV_MFMA_LAUNCH(false);
+        }
 #undef PKV_MFMA_LAUNCH
     } else {
+        if (a.slots) {
+            // Other dtypes and head sizes: the store kernel, then attention.
+            if (a.paged) return hipErrorInvalidValue;
+            const int es = dtype == 1 ? 2 : 4;
+            StoreArgs sa;
+            sa.k = (const uint8_t *)a.k;
+            sa.v = (const uint8_t *)a.v;
+            sa.k_stride_bytes = sa.v_stride_bytes = a.kv_stride * es;
+            sa.kc = (uint8_t *)a.store_kc;
+            sa.vc = (uint8_t *)a.store_vc;
+            sa.slots = a.slots;
+            sa.num_tokens = a.total_q;
+            sa.chunks_per_row = a.Hkv * a.d * es / 16;
+            sa.num_slots = a.num_slots;
+            const hipError_t e = launch_store(sa, stream);
+            if (e != hipSuccess) return e;
+        }
         const dim3 grid((a.max_seqlen_q + 3) / 4, a.Hq, a.num_seqs);
         if (dtype == 0 && a.d == 64)
             hipLaunchKernelGGL((prefill_generic_kernel<float, 64>), grid, dim3(256), 0, stream, a);

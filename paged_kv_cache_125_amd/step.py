@@ -13,7 +13,7 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 
 from . import (decode_attention_paged, decode_workspace_bytes, pack_decode, pack_prefill,
-               prefill_attention_varlen, store_kvcache)
+               prefill_attention_varlen, prefill_store_attention_varlen, store_kvcache)
 
 
 def alloc_pool(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
@@ -49,6 +49,7 @@ class StepInputs:
     scale: float
     use_block_tables: bool = True
     partition_size: int = 0
+    fuse_store: bool = False
 
 
 def run_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -57,7 +58,8 @@ def run_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
     """Pack + store + attention for one step. Decode: one new token per
     sequence (num_cached = len - 1). Prefill: keys read from the pool through
     the block tables when the batch has a cached prefix (or when
-    ``use_block_tables``), else from this step's contiguous k/v."""
+    ``use_block_tables``), else from this step's contiguous k/v -- then, with
+    ``fuse_store``, the store and the attention are one call."""
     dev = k_cache.device
     if s.phase == "decode":
         meta = pack_decode(s.seq_lens, s.block_tables, s.block_size, device=dev, stream=stream)
@@ -68,6 +70,10 @@ def run_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
                                       workspace=workspace, stream=stream)
     meta = pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size, device=dev,
                         stream=stream)
+    if s.fuse_store and meta["block_tables"] is None and not s.use_block_tables:
+        return prefill_store_attention_varlen(q, k_new, v_new, k_cache, v_cache, meta["slot_mapping"],
+                                              meta["cu_seqlens_q"], meta["max_seqlen_q"], s.scale,
+                                              out=out, stream=stream)
     store_kvcache(k_new, v_new, k_cache, v_cache, meta["slot_mapping"], stream=stream)
     bt = meta["block_tables"]
     if bt is None and s.use_block_tables:
@@ -133,9 +139,9 @@ def run_mixed_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: t
     return out
 
 
-def step_inputs_of(w, partition_size: int = 0) -> StepInputs:
+def step_inputs_of(w, partition_size: int = 0, fuse_store: bool = False) -> StepInputs:
     """StepInputs from any object with the batch fields (e.g. a seeded workload)."""
     return StepInputs(phase=w.phase, seq_lens=list(w.seq_lens), num_cached=list(w.num_cached),
                       block_tables=[list(t) for t in w.block_tables], block_size=w.block_size,
                       scale=w.scale, use_block_tables=w.use_block_tables,
-                      partition_size=partition_size)
+                      partition_size=partition_size, fuse_store=fuse_store)

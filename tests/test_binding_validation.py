@@ -111,6 +111,34 @@ def test_prefill_rejects_bad_out_and_stops_at_the_device_check():
         _prefill(_prefill_args(True))
 
 
+def _fused_args():
+    T, hq, hkv, d = 40, 4, 2, 128
+    return dict(q=torch.zeros(T, hq, d, dtype=BF), k=torch.zeros(T, hkv, d, dtype=BF),
+                v=torch.zeros(T, hkv, d, dtype=BF), k_cache=torch.zeros(5, 16, hkv, d, dtype=BF),
+                v_cache=torch.zeros(5, 16, hkv, d, dtype=BF), slot_mapping=torch.arange(T, dtype=I32),
+                cu_seqlens=torch.tensor([0, 15, 40], dtype=I32))
+
+
+@pytest.mark.parametrize("change, msg", [
+    (lambda a: a.update(k=a["k"].float(), v=a["v"].float()), "dtype"),    # fp32 rows, bf16 q and pool
+    (lambda a: a.update(k_cache=a["k_cache"].float()), "dtype"),
+    (lambda a: a.update(v=a["v"][:30]), "rows"),                          # fewer rows than q
+    (lambda a: a.update(slot_mapping=a["slot_mapping"][:39]), "entries"),  # a slot short
+    (lambda a: a.update(slot_mapping=a["slot_mapping"].long()), "int32"),
+    (lambda a: a.update(cu_seqlens=a["cu_seqlens"].long()), "int32"),
+    (lambda a: a.update(v_cache=torch.zeros(5, 16, 2, 64, dtype=BF)), "shape"),
+    (lambda a: a.update(k_cache=torch.zeros(5, 16, 2, 64, dtype=BF),
+                        v_cache=torch.zeros(5, 16, 2, 64, dtype=BF)), "head_dim"),
+])
+def test_fused_store_prefill_rejects_disagreeing_tensors(change, msg):
+    a = _fused_args()
+    change(a)
+    with pytest.raises(ValueError, match=msg):
+        pkv.prefill_store_attention_varlen(max_seqlen=25, scale=0.1, **a)
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.prefill_store_attention_varlen(max_seqlen=25, scale=0.1, **_fused_args())
+
+
 def _store_args():
     N, hkv, d = 7, 2, 128
     return dict(k=torch.zeros(N, hkv, d, dtype=BF), v=torch.zeros(N, hkv, d, dtype=BF),

@@ -1,0 +1,167 @@
+"""GPU tests of prefill_store_attention_varlen: store_kvcache and varlen
+attention over the call's own K/V rows (no cached prefix) in one call.
+
+Against the oracle: the pools bit for bit (history, then this call's rows at
+their slots) and every output row within the attention tolerance. Against
+the two separate calls on the GPU (store_kvcache, then prefill with keys from
+k/v): outputs and pools bit-identical, since the attention arithmetic is the
+same kernel's. Cases: the varlen preset in full, ragged lengths with one-row
+tails and single-token sequences, GQA groups 1 to 16, block sizes 1 to 256,
+padding slots (-1) and slots past the pool (skipped), an fp32 head_dim-64
+batch (store kernel, then attention), and an empty batch."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_125_amd as pkv
+from gpu_helpers import max_abs_err, raw, say, to_device
+from paged_kv_cache_125_amd.step import alloc_pool, run_step, step_inputs_of, write_ranges
+from workloads import custom_workload, make_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv.lib()
+    return torch.device("cuda")
+
+
+def _pools(w):
+    kc, vc = alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype, "cuda")
+    write_ranges(w.hist, w.block_tables, w.block_size, w.k_hist, w.v_hist, kc, vc)
+    return kc, vc
+
+
+def _fused(w, slots=None):
+    """One fused call; ``slots`` replaces the packed slot_mapping."""
+    kc, vc = _pools(w)
+    meta = pkv.pack_prefill(w.seq_lens, w.num_cached, w.block_tables, w.block_size, device="cuda")
+    assert meta["block_tables"] is None
+    sm = meta["slot_mapping"] if slots is None else slots
+    out = pkv.prefill_store_attention_varlen(w.q, w.k_new, w.v_new, kc, vc, sm, meta["cu_seqlens_q"],
+                                             meta["max_seqlen_q"], w.scale)
+    torch.cuda.synchronize()
+    return out, kc, vc, meta
+
+
+def _separate(w, slots=None):
+    """store_kvcache, then prefill over k/v: the two calls the fused one stands for."""
+    kc, vc = _pools(w)
+    meta = pkv.pack_prefill(w.seq_lens, w.num_cached, w.block_tables, w.block_size, device="cuda")
+    sm = meta["slot_mapping"] if slots is None else slots
+    pkv.store_kvcache(w.k_new, w.v_new, kc, vc, sm)
+    out = pkv.prefill_attention_varlen(w.q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                       meta["max_seqlen_q"], meta["max_seqlen_k"], w.scale,
+                                       k=w.k_new, v=w.v_new)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+def _check_against_oracle_and_separate(w):
+    wd = to_device(w, "cuda")
+    out, kc, vc, _ = _fused(wd)
+    want, kp, vp, _ = oracle.run_workload(w)
+    assert np.array_equal(raw(kc), raw(kp)), "k pool differs from the oracle's"
+    assert np.array_equal(raw(vc), raw(vp)), "v pool differs from the oracle's"
+    err = max_abs_err(out, want)
+    say(f"  max |err| = {err:.3e}")
+    assert err <= TOL[w.dtype]
+    out2, kc2, vc2 = _separate(wd)
+    assert torch.equal(out, out2), "fused output differs from store + prefill"
+    assert torch.equal(raw_t(kc), raw_t(kc2)) and torch.equal(raw_t(vc), raw_t(vc2))
+
+
+def raw_t(x: torch.Tensor) -> torch.Tensor:
+    return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+
+
+@pytest.mark.parametrize("preset", [(3, None), (1, "prefill")], ids=["preset3", "preset1-fp32"])
+def test_fused_store_presets(cuda, preset):
+    say(f"[gpu] fused store + prefill, preset {preset}")
+    w = make_workload(*preset)
+    assert not w.use_block_tables and all(c == 0 for c in w.num_cached)
+    _check_against_oracle_and_separate(w)
+
+
+CASES = [
+    # (lens, Hq, Hkv, bs)
+    ([257, 33], 12, 4, 16),                    # group 3, a one-row tail past two query blocks
+    ([1], 8, 8, 16),                           # one token, group 1
+    ([5, 130, 64], 4, 1, 4),                   # MQA, blocks of 4
+    ([128, 129, 127, 300], 16, 8, 1),          # block boundaries at every row, blocks of 1
+    ([1100, 300], 32, 2, 256),                 # group 16
+    ([1, 2, 3, 31, 32, 33, 63, 64, 65], 32, 4, 32),   # lengths around the wave and tile sizes, group 8
+    ([2048, 17], 16, 8, 64),                   # a long prompt beside a short one
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"fs{i}" for i in range(len(CASES))])
+def test_fused_store_shapes(cuda, case):
+    lens, hq, hkv, bs = case
+    say(f"[gpu] fused store + prefill {case}")
+    w = custom_workload(phase="prefill", seq_lens=lens, num_cached=[0] * len(lens), num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=128, block_size=bs, dtype=torch.bfloat16,
+                        seed=sum(lens) + 11 * bs, use_block_tables=False)
+    _check_against_oracle_and_separate(w)
+
+
+def test_fused_store_skips_padding_and_out_of_pool_slots(cuda):
+    say("[gpu] fused store: slots -1 and past the pool are skipped")
+    w = custom_workload(phase="prefill", seq_lens=[300, 77, 129], num_cached=[0, 0, 0], num_q_heads=8,
+                        num_kv_heads=2, head_dim=128, block_size=16, dtype=torch.bfloat16, seed=5,
+                        use_block_tables=False)
+    wd = to_device(w, "cuda")
+    meta = pkv.pack_prefill(w.seq_lens, w.num_cached, w.block_tables, w.block_size, device="cuda")
+    sm = meta["slot_mapping"].clone()
+    n = sm.numel()
+    pad = torch.arange(0, n, 5, device="cuda")
+    sm[pad] = -1
+    out, kc, vc, _ = _fused(wd, sm)
+    # the oracle with the same padding: the pools after this call's writes
+    kp = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, oracle.BF16)
+    vp = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, oracle.BF16)
+    ids = sm.cpu().numpy().astype(np.int64)
+    oracle.store(w.k_new, kp, ids)
+    oracle.store(w.v_new, vp, ids)
+    assert np.array_equal(raw(kc), raw(kp)) and np.array_equal(raw(vc), raw(vp))
+    want = oracle.attention(w.q, w.q_lens, w.seq_lens, w.num_kv_heads, w.scale, k=w.k_new, v=w.v_new)
+    assert max_abs_err(out, want) <= TOL[w.dtype]
+    # slots past the pool: skipped by both paths alike
+    num_slots = w.num_blocks * w.block_size
+    sm2 = meta["slot_mapping"].clone()
+    sm2[1::7] = num_slots + 3
+    out_f, kc_f, vc_f, _ = _fused(wd, sm2)
+    out_s, kc_s, vc_s = _separate(wd, sm2)
+    assert torch.equal(out_f, out_s)
+    assert torch.equal(raw_t(kc_f), raw_t(kc_s)) and torch.equal(raw_t(vc_f), raw_t(vc_s))
+
+
+def test_fused_store_through_run_step(cuda):
+    say("[gpu] run_step with fuse_store on the varlen preset equals the unfused step")
+    w = to_device(make_workload(3), "cuda")
+    outs = []
+    for fuse in (False, True):
+        kc, vc = _pools(w)
+        outs.append((run_step(step_inputs_of(w, fuse_store=fuse), w.q, w.k_new, w.v_new, kc, vc), kc, vc))
+    torch.cuda.synchronize()
+    (o0, k0, v0), (o1, k1, v1) = outs
+    assert torch.equal(o0, o1)
+    assert torch.equal(raw_t(k0), raw_t(k1)) and torch.equal(raw_t(v0), raw_t(v1))
+
+
+def test_fused_store_empty_batch(cuda):
+    say("[gpu] fused store: an empty batch is a no-op")
+    kc = torch.zeros((4, 16, 2, 128), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    q = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sm = torch.zeros(0, dtype=torch.int32, device="cuda")
+    out = pkv.prefill_store_attention_varlen(q, kv, kv, kc, vc, sm, cu, 0, 0.088)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 8, 128) and not kc.any() and not vc.any()
