@@ -4,7 +4,10 @@ groups (including 3 and 6), head_dim (64, 128), dtype (bf16, fp32), block
 size (1..512) and forced partition size are drawn from fixed seeds, so that
 combinations no hand-picked edge case spans are exercised. Each case is small
 enough for the oracle; the tolerance is the attention bar (2e-2 bf16, 1e-4
-fp32) and the pools are compared bit for bit."""
+fp32) and the pools are compared bit for bit. The prefill shapes are also run
+without a cached prefix through prefill_store_attention_varlen, which must
+match the oracle and equal the separate store and attention calls bit for
+bit."""
 import numpy as np
 import pytest
 import torch
@@ -12,6 +15,7 @@ import torch
 import oracle
 import paged_kv_cache_125_amd as pkv
 from gpu_helpers import gpu_run, max_abs_err, raw, say, to_device
+from paged_kv_cache_125_amd.step import alloc_pool
 from workloads import custom_workload
 
 pytestmark = pytest.mark.gpu
@@ -84,3 +88,27 @@ def test_random_prefill(cuda, i):
     err = max_abs_err(out, want)
     say(f"  max |err| = {err:.3e}")
     assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("i", range(N_CASES), ids=lambda i: f"fs-r{i}")
+def test_random_fused_store_prefill(cuda, i):
+    lens, _, hq, hkv, d, dt, bs = prefill_case(i)
+    say(f"[gpu] random fused store + prefill {i}: lens {lens} Hq {hq} Hkv {hkv} d {d} {dt} bs {bs}")
+    w = custom_workload(phase="prefill", seq_lens=lens, num_cached=[0] * len(lens), num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dt, seed=190 + i,
+                        use_block_tables=False)
+    wd = to_device(w, "cuda")
+    out, kc, vc = gpu_run(wd)   # store_kvcache, then prefill over k/v
+    kf, vf = alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype, "cuda")
+    meta = pkv.pack_prefill(w.seq_lens, w.num_cached, w.block_tables, w.block_size, device="cuda")
+    of = pkv.prefill_store_attention_varlen(wd.q, wd.k_new, wd.v_new, kf, vf, meta["slot_mapping"],
+                                            meta["cu_seqlens_q"], meta["max_seqlen_q"], w.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw(of), raw(out)), "fused output differs from the separate calls"
+    assert np.array_equal(raw(kf), raw(kc)) and np.array_equal(raw(vf), raw(vc))
+    want, kp, vp, _ = oracle.run_workload(w)
+    assert np.array_equal(raw(kf), raw(kp)) and np.array_equal(raw(vf), raw(vp))
+    err = max_abs_err(of, want)
+    say(f"  max |err| = {err:.3e}")
+    assert err <= TOL[dt]
+
