@@ -68,8 +68,10 @@ WORKLOADS = {
     "mixed": [("prefill", 7), ("prefill+split", 7)],
     # preset 3's step with the rotary embedding fused into the store
     "rope-store": [("prefill+rope", 3)],
-    # preset 3's store and attention as two calls, then as one fused call
+    # store and attention as two calls, then as one fused call: preset 3
+    # (keys are the call's rows), preset 4 (prefix hits through the pool)
     "fused-store": [("prefill", 3), ("prefill+fused", 3)],
+    "fused-store-prefix": [("prefill", 4), ("prefill+fused", 4)],
     # preset 2's decode, plus 28-layer decode steps eager vs replayed hipGraphs
     "decode-graph": [("decode", 2)],
 }
@@ -264,8 +266,9 @@ class Part:
             if self.fused:
                 rec(2)
                 pkv.prefill_store_attention_varlen(w.q, w.k_new, w.v_new, kc, vc, meta["slot_mapping"],
-                                                   meta["cu_seqlens_q"], meta["max_seqlen_q"], s.scale,
-                                                   out=out)
+                                                   meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                                   meta["max_seqlen_q"], meta["max_seqlen_k"], s.scale,
+                                                   block_tables=meta["block_tables"], out=out)
                 rec(3)
                 return meta
             if self.rope:

@@ -169,43 +169,52 @@ size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q, int32
 
 /* ---------------------------------------------------------------------------
  * prefill_store_attention_varlen: store_kvcache and prefill_attention_varlen
- * of a batch with no cached prefix, in one call ([MR] the attention layer's
- * forward, which writes the step's K/V through slot_mapping and then runs
- * varlen attention over them; "prepare_prefill" for the metadata).
+ * of one prefill step in one call ([MR] the attention layer's forward, which
+ * writes the step's K/V through slot_mapping and then runs varlen attention;
+ * "prepare_prefill" for the metadata; [NV1] "5. deocde 输入打包" for the
+ * block tables on a prefix hit).
  *
  * The result equals pkv_store_kvcache(k, v, kv_token_stride, kv_token_stride,
  * k_cache, v_cache, slot_mapping, total_q, num_blocks, block_size, ...)
- * followed on the same stream by pkv_prefill_attention_varlen with
- * block_tables == NULL and cu_seqlens_q == cu_seqlens_k == cu_seqlens: the
- * keys of sequence s are its own rows [cu_seqlens[s], cu_seqlens[s+1]) of k/v
- * (Lk_s == Lq_s), and row i of k/v is also written to cache slot
- * slot_mapping[i] (skipped when negative or past the pool).
+ * followed on the same stream by pkv_prefill_attention_varlen(q, ..., k, v,
+ * kv_token_stride, k_cache, v_cache, block_tables, ...) with the same
+ * arguments, provided the metadata agree the way pkv_pack_prefill lays them
+ * out:
+ *  - block_tables == NULL: the keys of sequence s are its own rows of k/v
+ *    (Lk_s == Lq_s), as in pkv_prefill_attention_varlen.
+ *  - block_tables != NULL: positions below Lk_s - Lq_s are read from the
+ *    caches through the block table; the later ones -- the tokens this call
+ *    stores -- are read from the call's rows, position Lk_s - Lq_s + i from
+ *    row cu_seqlens_q[s] + i, instead of from the slots they are stored to.
+ *    The two forms agree when slot_mapping[cu_seqlens_q[s] + i] is the slot
+ *    of that position under sequence s's block table.
  *
- * For bf16 and head_dim 128 this is one launch: after its attention, the
- * workgroup of each query block that serves the first query head of a kv head
- * copies that block's K/V rows into their slots (the rows were loaded for the
- * block's last key tiles moments before). Other dtypes and head sizes run the
+ * For bf16 and head_dim 128 (block_size >= 4 with block tables) this is one
+ * launch: after its attention, each query block copies its own rows of k/v
+ * into their slots (the group's query heads share the copy; the rows were
+ * read for the block's last key tiles moments before). Other shapes run the
  * store kernel and then the attention kernel. Rows outside every sequence's
- * range, and rows of a sequence the attention skips (see above), may be left
- * unstored; with cu_seqlens a prefix sum from 0 to total_q (what
- * pkv_pack_prefill writes) every row is stored. The cache writes are not read
- * by this call, so k/v and the caches may be any distinct buffers.
+ * range, and rows of a sequence the attention skips (see
+ * pkv_prefill_attention_varlen), may be left unstored; with metadata from
+ * pkv_pack_prefill every row is stored. The call reads no slot it writes.
  *
- *  q, out          as in pkv_prefill_attention_varlen.
+ *  q, out, cu_seqlens_q/_k, max_seqlen_q/_k, block_tables, max_blocks_per_seq:
+ *                  as in pkv_prefill_attention_varlen.
  *  k, v            [total_q, num_kv_heads, head_dim], token stride
- *                  kv_token_stride, q's dtype.
+ *                  kv_token_stride, q's dtype; row i is the token of q row i.
  *  k_cache,v_cache [num_blocks, block_size, num_kv_heads, head_dim].
- *  slot_mapping    device int32 [total_q]; slots unique within the call.
- *  cu_seqlens      device int32 [num_seqs + 1]; max_seqlen bounds Lq_s.
- * Errors as in the two calls it combines; the pool shape only sizes the slot
- * range (num_blocks * block_size <= 2^31 - 1, block_size any positive value).
- * Uses no workspace (always the one-workgroup-per-item grid). */
+ *  slot_mapping    device int32 [total_q]; slots unique within the call;
+ *                  negative slots and slots past the pool are skipped.
+ * Errors as in the two calls it combines. Uses no workspace (always one
+ * workgroup per item). */
 int pkv_prefill_store_attention_varlen(const void *q, int64_t q_token_stride, const void *k,
                                        const void *v, int64_t kv_token_stride, void *k_cache,
                                        void *v_cache, const int32_t *slot_mapping,
-                                       int32_t num_blocks, int32_t block_size,
-                                       const int32_t *cu_seqlens, int32_t num_seqs,
-                                       int32_t total_q, int32_t max_seqlen, int32_t num_q_heads,
+                                       const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                       int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                       int32_t max_seqlen_k, int32_t num_blocks,
+                                       int32_t block_size, int32_t num_q_heads,
                                        int32_t num_kv_heads, int32_t head_dim, float scale,
                                        int32_t dtype, void *out, void *stream);
 

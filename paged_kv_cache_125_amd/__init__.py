@@ -86,8 +86,8 @@ def lib():
     L.pkv_prefill_attention_varlen.argtypes = [P, i64, P, P, i64, P, P, P, i32, P, P, i32, i32, i32,
                                                i32, i32, i32, i32, i32, i32, f32, i32, P, P, sz, P]
     L.pkv_prefill_store_attention_varlen.restype = ctypes.c_int
-    L.pkv_prefill_store_attention_varlen.argtypes = [P, i64, P, P, i64, P, P, P, i32, i32, P, i32, i32,
-                                                     i32, i32, i32, i32, f32, i32, P, P]
+    L.pkv_prefill_store_attention_varlen.argtypes = [P, i64, P, P, i64, P, P, P, P, i32, P, P, i32, i32,
+                                                     i32, i32, i32, i32, i32, i32, i32, f32, i32, P, P]
     L.pkv_prefill_workspace_bytes.restype = sz
     L.pkv_prefill_workspace_bytes.argtypes = [i32] * 6
     L.pkv_decode_attention_paged.restype = ctypes.c_int
@@ -470,14 +470,15 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
 
 def prefill_store_attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                    k_cache: torch.Tensor, v_cache: torch.Tensor,
-                                   slot_mapping: torch.Tensor, cu_seqlens: torch.Tensor,
-                                   max_seqlen: int, scale: float, *,
-                                   out: Optional[torch.Tensor] = None,
-                                   stream=None) -> torch.Tensor:
+                                   slot_mapping: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                   cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                                   scale: float, *, block_tables: Optional[torch.Tensor] = None,
+                                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """pkv_prefill_store_attention_varlen: store_kvcache(k, v, k_cache, v_cache,
-    slot_mapping) and prefill_attention_varlen over the call's own k/v rows
-    (no cached prefix; cu_seqlens serves as both cu_seqlens_q and _k), in one
-    launch on the bf16 head_dim-128 path."""
+    slot_mapping) and prefill_attention_varlen in one launch on the bf16
+    head_dim-128 path. Without ``block_tables`` the keys are the call's own
+    k/v rows; with them, cached positions come from the pool and this call's
+    positions from its k/v rows."""
     _need(q.dim() == 3, "q must be [tokens, num_q_heads, head_dim]")
     _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
     total_q, hq, d = q.shape
@@ -491,18 +492,26 @@ def prefill_store_attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Te
     if _token_stride(v) != kv_stride:
         raise ValueError("k and v must share a token stride")
     _int32_vec(slot_mapping, "slot_mapping", total_q)
-    _int32_vec(cu_seqlens, "cu_seqlens", 1)
-    num_seqs = int(cu_seqlens.numel()) - 1
+    _int32_vec(cu_seqlens_q, "cu_seqlens_q", 1)
+    _int32_vec(cu_seqlens_k, "cu_seqlens_k", 1)
+    _need(cu_seqlens_k.numel() == cu_seqlens_q.numel(),
+          "cu_seqlens_q and cu_seqlens_k must have one entry per sequence plus one")
+    num_seqs = int(cu_seqlens_q.numel()) - 1
+    maxb = 0
+    if block_tables is not None:
+        _int32_table(block_tables, "block_tables", num_seqs)
+        maxb = int(block_tables.shape[1])
     if out is not None:
         _out(out, q)
     _one_gpu(q=q, k=k, v=v, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping,
-             cu_seqlens=cu_seqlens, out=out)
+             cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, block_tables=block_tables, out=out)
     if out is None:
         out = _alloc_on(stream, (total_q, hq, d), dtype=q.dtype, device=q.device)
     _check(lib().pkv_prefill_store_attention_varlen(
         _ptr(q), _token_stride(q), _ptr(k), _ptr(v), kv_stride, _ptr(k_cache), _ptr(v_cache),
-        _ptr(slot_mapping), nb, bs, _ptr(cu_seqlens), num_seqs, total_q, int(max_seqlen), hq, hkv,
-        d, float(scale), _dtype_code(q), _ptr(out), _stream(stream)))
+        _ptr(slot_mapping), _ptr(block_tables), maxb, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        num_seqs, total_q, int(max_seqlen_q), int(max_seqlen_k), nb, bs, hq, hkv, d, float(scale),
+        _dtype_code(q), _ptr(out), _stream(stream)))
     return out
 
 

@@ -236,9 +236,12 @@ static int prefill_call(
     if (a.paged) {
         rc = check_pool(fn, k_cache, v_cache, block_tables, max_blocks_per_seq, num_blocks, block_size);
         if (rc) return rc;
+    }
+    if (a.paged && !st) {
         a.k = a.v = nullptr;
         a.kv_stride = 0;
     } else {
+        // the keys' rows (no block tables), or the rows the fused store writes
         if (!k || !v) return fail(PKV_EINVAL, "%s: null k/v without block tables", fn);
         if (kv_token_stride < (int64_t)num_kv_heads * head_dim)
             return fail(PKV_EINVAL, "%s: kv token stride smaller than a row", fn);
@@ -300,10 +303,11 @@ extern "C" int pkv_prefill_attention_varlen(
 
 extern "C" int pkv_prefill_store_attention_varlen(
     const void *q, int64_t q_token_stride, const void *k, const void *v, int64_t kv_token_stride,
-    void *k_cache, void *v_cache, const int32_t *slot_mapping, int32_t num_blocks,
-    int32_t block_size, const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_q,
-    int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
-    int32_t dtype, void *out, void *stream) {
+    void *k_cache, void *v_cache, const int32_t *slot_mapping, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+    int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_blocks, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t dtype, void *out, void *stream) {
     const char *fn = "pkv_prefill_store_attention_varlen";
     if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
     if (block_size <= 0 || num_blocks <= 0) return fail(PKV_EINVAL, "%s: non-positive pool shape", fn);
@@ -311,14 +315,18 @@ extern "C" int pkv_prefill_store_attention_varlen(
     if (num_slots > INT32_MAX) return fail(PKV_EINVAL, "%s: pool has more than 2^31-1 slots", fn);
     if (num_kv_heads > 0 && head_dim > 0 && ((int64_t)num_kv_heads * head_dim * elem_size(dtype)) % 16)
         return fail(PKV_EUNSUPPORTED, "%s: row bytes not a multiple of 16", fn);
-    if (total_q > 0 && num_seqs > 0 && max_seqlen > 0) {
+    if (total_q > 0 && num_seqs > 0 && max_seqlen_q > 0) {
+        if (!k || !v) return fail(PKV_EINVAL, "%s: null k/v", fn);
         if (!k_cache || !v_cache || !slot_mapping) return fail(PKV_EINVAL, "%s: null cache or slot_mapping", fn);
         if (!aligned16(k_cache) || !aligned16(v_cache))
             return fail(PKV_EINVAL, "%s: caches must be 16-byte aligned", fn);
     }
     const PrefillStore st = {k_cache, v_cache, slot_mapping, (int32_t)num_slots};
-    return prefill_call(fn, q, q_token_stride, k, v, kv_token_stride, nullptr, nullptr, nullptr, 0,
-                        cu_seqlens, cu_seqlens, num_seqs, total_q, max_seqlen, max_seqlen,
+    // With block tables the attention reads the pool and the call's k/v rows
+    // both; without, only the rows.
+    return prefill_call(fn, q, q_token_stride, k, v, kv_token_stride, block_tables ? k_cache : nullptr,
+                        block_tables ? v_cache : nullptr, block_tables, max_blocks_per_seq,
+                        cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, max_seqlen_q, max_seqlen_k,
                         num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, scale, dtype,
                         out, nullptr, 0, &st, stream);
 }

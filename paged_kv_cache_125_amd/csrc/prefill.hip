@@ -87,13 +87,13 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __attribute__
 
 // NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
 // owns BM = 32 * RB * NW rows of one query head. WPE waves share one SIMD.
-// STORE (contiguous keys only): the workgroups of the first query head of
-// each kv head also copy their query block's own K/V rows into the cache
-// (store_kvcache fused into the attention launch).
+// STORE: store_kvcache fused into the attention launch. Each query block
+// also copies its own rows of the call's k/v into the cache (shared out over
+// the group's query heads), and keys at positions Lk - Lq and beyond -- the
+// ones this call stores -- are read from those rows rather than the pool.
 template <int SRC, int NW, int RB, int WPE, bool PERSIST, bool STORE>
 __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
-    static_assert(!STORE || (SRC == kContiguous && RB == 1 && !PERSIST),
-                  "the fused store is built for the fixed grid over contiguous keys");
+    static_assert(!STORE || (RB == 1 && !PERSIST), "the fused store is built for the fixed grid");
     constexpr int BM = 32 * RB * NW;         // query rows per workgroup (one query head)
     constexpr int LPW = 16 / NW;   // 1 KiB direct-load instructions per wave per K (or V) tile
     static_assert(NW * LPW == 16 && NW >= 2, "waves must split a tile evenly");
@@ -197,11 +197,11 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
             qb[rb][kk] = __builtin_bit_cast(bf16x8, w);
         }
     }
-    // Fused store: the cache slot of the wave's row r32 (key row == query row
-    // with contiguous keys), loaded with q; -1 for rows past the sequence.
+    // Fused store: the cache slot of the wave's row r32 (row i of q, k and v
+    // is the same token), loaded with q; -1 for rows past the sequence.
     int my_slot = -1;
     if constexpr (STORE) {
-        if (row_ok[0]) my_slot = a.slots[k_start + q0 + 32 * wh + r32];
+        if (row_ok[0]) my_slot = a.slots[q_start + q0 + 32 * wh + r32];
     }
     const int kend = min(Lk, off + min(q0 + BM, Lq));   // keys this block needs
     const int n_kt = (kend + kPfBN - 1) / kPfBN;
@@ -251,9 +251,93 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
                                     : t * (int)stride_b + 16 * chunk - 1024 * i;
     }
     typedef __attribute__((address_space(3))) void lds_t;
+    // Fused store over the pool: keys at positions off and beyond come from
+    // the call's k/v rows (position p is row q_start + p - off), the rows
+    // this call stores; the others from the pool. voff_n is voff for those
+    // rows' stride.
+    const uint8_t *knbase = (const uint8_t *)a.k + (int64_t)kvh * kPfD * 2;
+    const uint8_t *vnbase = (const uint8_t *)a.v + (int64_t)kvh * kPfD * 2;
+    const uint32_t stride_n = (uint32_t)(a.kv_stride * 2);
+    int voff_n[8];
+    if constexpr (STORE && SRC != kContiguous) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int t = 4 * (LPW * wave + i) + (lane >> 4);
+            const int chunk = (lane & 15) ^ tile_swz(t);
+            voff_n[i] = SRC == kPoolSmall ? (lane >> 4) * (int)stride_n + 16 * chunk
+                                          : t * (int)stride_n + 16 * chunk - 1024 * i;
+        }
+    }
+    // Descriptor over the call's rows from key `key0` on (the base may lie
+    // before the sequence's first row when key0 < off: only lanes at keys
+    // off and beyond use it), nk keys long.
+    auto rows_rsrc = [&](const uint8_t *base, int key0, int nk) {
+        const int nrec = __builtin_amdgcn_readfirstlane(max(0, nk) * (int)stride_n);
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(base + ((int64_t)q_start + key0 - off) * stride_n), (short)0, nrec, kBufWord3);
+    };
     auto load_tile = [&](int k0, uint8_t *dst) {
         uint8_t *kd = dst + 1024 * LPW * wave;
         uint8_t *vd = dst + kTileBytes + 1024 * LPW * wave;
+        if constexpr (STORE && SRC != kContiguous) {
+            if (k0 >= off) {
+                // every key of the tile is this call's: its rows, as in the contiguous form
+                const int nkeys = min(kPfBN, kend - k0);
+                if constexpr (SRC == kPoolSmall) {
+#pragma unroll
+                    for (int i = 0; i < LPW; ++i) {
+                        const int key0 = k0 + 4 * (LPW * wave + i);
+                        const int nk = min(4, kend - key0);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(knbase, key0, nk), (lds_t *)(kd + 1024 * i), 16, voff_n[i], 0, 0, 0);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(vnbase, key0, nk), (lds_t *)(vd + 1024 * i), 16, voff_n[i], 0, 0, 0);
+                    }
+                } else {
+                    dma_tile(rows_rsrc(knbase, k0, nkeys), (lds_t *)kd, voff_n, std::make_integer_sequence<int, LPW>{});
+                    dma_tile(rows_rsrc(vnbase, k0, nkeys), (lds_t *)vd, voff_n, std::make_integer_sequence<int, LPW>{});
+                }
+                return;
+            }
+            if (k0 + kPfBN > off) {
+                // The tile holds both (at most one such tile per item): each
+                // load goes out twice with complementary lane masks, cached
+                // keys from the pool and the rest from the rows. Masked-off
+                // lanes neither read nor write LDS.
+                const int nkeys = min(kPfBN, kend - k0);
+#pragma unroll
+                for (int i = 0; i < LPW; ++i) {
+                    const int t = 4 * (LPW * wave + i) + (lane >> 4);
+                    const int chunk = (lane & 15) ^ tile_swz(t);
+                    const int key0 = k0 + 4 * (LPW * wave + i);
+                    int blk, prow, np;   // the cached keys' block, pool row of the base, keys in range
+                    if constexpr (SRC == kPoolSmall) {
+                        blk = pre_blk[i];
+                        prow = key0 & (a.bs - 1);
+                        np = min(4, off - key0);
+                    } else {
+                        blk = pre_blk[0];
+                        prow = k0 & (a.bs - 1);
+                        np = off - k0;
+                    }
+                    const bool ok = (uint32_t)blk < (uint32_t)a.num_blocks;
+                    const int nrec = __builtin_amdgcn_readfirstlane(ok ? max(0, np) * (int)stride_b : 0);
+                    const int64_t rb_ = ((int64_t)(ok ? blk : 0) * a.bs + prow) * stride_b;
+                    const int vo_p = (SRC == kPoolSmall ? (lane >> 4) : t) * (int)stride_b + 16 * chunk;
+                    const int vo_n = t * (int)stride_n + 16 * chunk;
+                    if (k0 + t < off) {
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + rb_), (short)0, nrec, kBufWord3),
+                            (lds_t *)(kd + 1024 * i), 16, vo_p, 0, 0, 0);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + rb_), (short)0, nrec, kBufWord3),
+                            (lds_t *)(vd + 1024 * i), 16, vo_p, 0, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(knbase, k0, nkeys), (lds_t *)(kd + 1024 * i), 16, vo_n, 0, 0, 0);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(vnbase, k0, nkeys), (lds_t *)(vd + 1024 * i), 16, vo_n, 0, 0, 0);
+                    }
+                }
+                return;
+            }
+        }
         if constexpr (SRC == kPoolSmall) {
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
@@ -536,7 +620,7 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
                 if (i % HG == hg) {   // wave-uniform
                     slot[i] = __shfl(my_slot, rr);
                     if ((uint32_t)slot[i] < (uint32_t)a.num_slots) {
-                        const int64_t src = (int64_t)(k_start + rbase + rr) * a.kv_stride + kvh * kPfD + 8 * chunk;
+                        const int64_t src = (int64_t)(q_start + rbase + rr) * a.kv_stride + kvh * kPfD + 8 * chunk;
                         kw[i] = ld16((const uint16_t *)a.k + src);
                         vw[i] = ld16((const uint16_t *)a.v + src);
                     }
@@ -751,11 +835,11 @@ void prefill_mfma_kernel(PrefillArgs a) {
     prefill_mfma_body<SRC, NW, RB, WPE, PERSIST, false>(a);
 }
 
-// Contiguous keys with the call's K/V rows also stored into the cache.
-template <int NW, int WPE>
+// The call's K/V rows also stored into the cache.
+template <int SRC, int NW, int WPE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_store_mfma_kernel(PrefillArgs a) {
-    prefill_mfma_body<kContiguous, NW, 1, WPE, false, true>(a);
+    prefill_mfma_body<SRC, NW, 1, WPE, false, true>(a);
 }
 
 template <typename T>
@@ -847,7 +931,9 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
     // descriptor with 32-bit offsets, and the small-block form needs blocks of
     // at least 4 keys; anything else takes the generic kernel.
     const int64_t row_bytes = a.paged ? (int64_t)a.Hkv * a.d * 2 : a.kv_stride * 2;
-    if (dtype == 1 && a.d == 128 && (!a.paged || a.bs >= 4) && row_bytes * kPfBN < (1ll << 31)) {
+    // The fused store over the pool also addresses 64 of the call's rows.
+    const bool rows_ok = !(a.slots && a.paged) || a.kv_stride * 2 * kPfBN < (1ll << 31);
+    if (dtype == 1 && a.d == 128 && (!a.paged || a.bs >= 4) && row_bytes * kPfBN < (1ll << 31) && rows_ok) {
         // Four waves of 32 query rows per workgroup (one head, 128 rows), two
         // waves per SIMD: while one wave waits on LDS or runs its softmax the
         // other keeps the matrix core busy.
@@ -876,8 +962,13 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
             hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2, P>), grid, block, 0, stream, a);  \
     } while (0)
         if (a.slots) {
-            if (a.paged) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((prefill_store_mfma_kernel<NW, 2>), dim3((unsigned)nwg_fixed), block, 0, stream, a);
+            const dim3 g((unsigned)nwg_fixed);
+            if (!a.paged)
+                hipLaunchKernelGGL((prefill_store_mfma_kernel<kContiguous, NW, 2>), g, block, 0, stream, a);
+            else if (a.bs % kPfBN == 0)
+                hipLaunchKernelGGL((prefill_store_mfma_kernel<kPoolBlocks, NW, 2>), g, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((prefill_store_mfma_kernel<kPoolSmall, NW, 2>), g, block, 0, stream, a);
         } else if (persist) {
             PKV_MFMA_LAUNCH(true);
         } else {
@@ -886,8 +977,8 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
 #undef PKV_MFMA_LAUNCH
     } else {
         if (a.slots) {
-            // Other dtypes and head sizes: the store kernel, then attention.
-            if (a.paged) return hipErrorInvalidValue;
+            // Other dtypes, head sizes and block sizes: the store kernel, then
+            // attention (over the pool when there are block tables).
             const int es = dtype == 1 ? 2 : 4;
             StoreArgs sa;
             sa.k = (const uint8_t *)a.k;

@@ -58,8 +58,8 @@ def run_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
     """Pack + store + attention for one step. Decode: one new token per
     sequence (num_cached = len - 1). Prefill: keys read from the pool through
     the block tables when the batch has a cached prefix (or when
-    ``use_block_tables``), else from this step's contiguous k/v -- then, with
-    ``fuse_store``, the store and the attention are one call."""
+    ``use_block_tables``), else from this step's contiguous k/v. With
+    ``fuse_store`` the store and the attention are one call."""
     dev = k_cache.device
     if s.phase == "decode":
         meta = pack_decode(s.seq_lens, s.block_tables, s.block_size, device=dev, stream=stream)
@@ -70,16 +70,17 @@ def run_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
                                       workspace=workspace, stream=stream)
     meta = pack_prefill(s.seq_lens, s.num_cached, s.block_tables, s.block_size, device=dev,
                         stream=stream)
-    if s.fuse_store and meta["block_tables"] is None and not s.use_block_tables:
-        return prefill_store_attention_varlen(q, k_new, v_new, k_cache, v_cache, meta["slot_mapping"],
-                                              meta["cu_seqlens_q"], meta["max_seqlen_q"], s.scale,
-                                              out=out, stream=stream)
-    store_kvcache(k_new, v_new, k_cache, v_cache, meta["slot_mapping"], stream=stream)
     bt = meta["block_tables"]
     if bt is None and s.use_block_tables:
         # a batch without a cached prefix may still read its keys from the pool
         meta_bt = pack_decode(s.seq_lens, s.block_tables, s.block_size, device=dev, stream=stream)
         bt = meta_bt["block_tables"]
+    if s.fuse_store:
+        return prefill_store_attention_varlen(q, k_new, v_new, k_cache, v_cache, meta["slot_mapping"],
+                                              meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                              meta["max_seqlen_q"], meta["max_seqlen_k"], s.scale,
+                                              block_tables=bt, out=out, stream=stream)
+    store_kvcache(k_new, v_new, k_cache, v_cache, meta["slot_mapping"], stream=stream)
     if bt is not None:
         return prefill_attention_varlen(q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
                                         meta["max_seqlen_q"], meta["max_seqlen_k"], s.scale,

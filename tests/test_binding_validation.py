@@ -116,7 +116,8 @@ def _fused_args():
     return dict(q=torch.zeros(T, hq, d, dtype=BF), k=torch.zeros(T, hkv, d, dtype=BF),
                 v=torch.zeros(T, hkv, d, dtype=BF), k_cache=torch.zeros(5, 16, hkv, d, dtype=BF),
                 v_cache=torch.zeros(5, 16, hkv, d, dtype=BF), slot_mapping=torch.arange(T, dtype=I32),
-                cu_seqlens=torch.tensor([0, 15, 40], dtype=I32))
+                cu_seqlens_q=torch.tensor([0, 15, 40], dtype=I32),
+                cu_seqlens_k=torch.tensor([0, 15, 40], dtype=I32))
 
 
 @pytest.mark.parametrize("change, msg", [
@@ -125,7 +126,10 @@ def _fused_args():
     (lambda a: a.update(v=a["v"][:30]), "rows"),                          # fewer rows than q
     (lambda a: a.update(slot_mapping=a["slot_mapping"][:39]), "entries"),  # a slot short
     (lambda a: a.update(slot_mapping=a["slot_mapping"].long()), "int32"),
-    (lambda a: a.update(cu_seqlens=a["cu_seqlens"].long()), "int32"),
+    (lambda a: a.update(cu_seqlens_q=a["cu_seqlens_q"].long()), "int32"),
+    (lambda a: a.update(cu_seqlens_k=torch.tensor([0, 40], dtype=I32)), "one entry"),
+    (lambda a: a.update(block_tables=torch.zeros(1, 3, dtype=I32)), "rows"),    # fewer rows than sequences
+    (lambda a: a.update(block_tables=torch.zeros(2, 3, dtype=torch.int64)), "int32"),
     (lambda a: a.update(v_cache=torch.zeros(5, 16, 2, 64, dtype=BF)), "shape"),
     (lambda a: a.update(k_cache=torch.zeros(5, 16, 2, 64, dtype=BF),
                         v_cache=torch.zeros(5, 16, 2, 64, dtype=BF)), "head_dim"),
@@ -134,9 +138,12 @@ def test_fused_store_prefill_rejects_disagreeing_tensors(change, msg):
     a = _fused_args()
     change(a)
     with pytest.raises(ValueError, match=msg):
-        pkv.prefill_store_attention_varlen(max_seqlen=25, scale=0.1, **a)
+        pkv.prefill_store_attention_varlen(max_seqlen_q=25, max_seqlen_k=25, scale=0.1, **a)
     with pytest.raises(ValueError, match="GPU"):
-        pkv.prefill_store_attention_varlen(max_seqlen=25, scale=0.1, **_fused_args())
+        pkv.prefill_store_attention_varlen(max_seqlen_q=25, max_seqlen_k=25, scale=0.1, **_fused_args())
+    with pytest.raises(ValueError, match="GPU"):
+        pkv.prefill_store_attention_varlen(max_seqlen_q=25, max_seqlen_k=25, scale=0.1,
+                                           block_tables=torch.zeros(2, 3, dtype=I32), **_fused_args())
 
 
 def _store_args():

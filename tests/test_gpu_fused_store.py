@@ -1,14 +1,18 @@
 """GPU tests of prefill_store_attention_varlen: store_kvcache and varlen
-attention over the call's own K/V rows (no cached prefix) in one call.
+attention in one call, with keys from the call's own K/V rows, or -- on a
+prefix hit -- cached positions from the pool and this call's positions from
+its rows.
 
 Against the oracle: the pools bit for bit (history, then this call's rows at
 their slots) and every output row within the attention tolerance. Against
-the two separate calls on the GPU (store_kvcache, then prefill with keys from
-k/v): outputs and pools bit-identical, since the attention arithmetic is the
-same kernel's. Cases: the varlen preset in full, ragged lengths with one-row
-tails and single-token sequences, GQA groups 1 to 16, block sizes 1 to 256,
-padding slots (-1) and slots past the pool (skipped), an fp32 head_dim-64
-batch (store kernel, then attention), and an empty batch."""
+the two separate calls on the GPU (store_kvcache, then prefill): outputs and
+pools bit-identical, since the attention arithmetic is the same kernel's and
+the key tiles hold the same bytes. Cases: the varlen and prefix-hit presets
+and the mixed batches in full; ragged lengths with one-row tails and single
+tokens; GQA groups 1 to 16; block sizes 1 to 256 (whole-tile blocks, 4-key
+groups, and the two-kernel form below 4); cached prefixes that end inside a
+tile and inside a 4-key group, decode rows (one new token); padding slots
+(-1) and slots past the pool; an fp32 head_dim-64 batch; an empty batch."""
 import numpy as np
 import pytest
 import torch
@@ -37,27 +41,41 @@ def _pools(w):
     return kc, vc
 
 
+def _bt(w, meta):
+    """The block tables the step reads through (also for a batch without a
+    cached prefix whose workload asks for them), or None."""
+    if meta["block_tables"] is not None or not w.use_block_tables:
+        return meta["block_tables"]
+    return pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cuda")["block_tables"]
+
+
 def _fused(w, slots=None):
     """One fused call; ``slots`` replaces the packed slot_mapping."""
     kc, vc = _pools(w)
     meta = pkv.pack_prefill(w.seq_lens, w.num_cached, w.block_tables, w.block_size, device="cuda")
-    assert meta["block_tables"] is None
     sm = meta["slot_mapping"] if slots is None else slots
     out = pkv.prefill_store_attention_varlen(w.q, w.k_new, w.v_new, kc, vc, sm, meta["cu_seqlens_q"],
-                                             meta["max_seqlen_q"], w.scale)
+                                             meta["cu_seqlens_k"], meta["max_seqlen_q"], meta["max_seqlen_k"],
+                                             w.scale, block_tables=_bt(w, meta))
     torch.cuda.synchronize()
     return out, kc, vc, meta
 
 
 def _separate(w, slots=None):
-    """store_kvcache, then prefill over k/v: the two calls the fused one stands for."""
+    """store_kvcache, then prefill: the two calls the fused one stands for."""
     kc, vc = _pools(w)
     meta = pkv.pack_prefill(w.seq_lens, w.num_cached, w.block_tables, w.block_size, device="cuda")
     sm = meta["slot_mapping"] if slots is None else slots
     pkv.store_kvcache(w.k_new, w.v_new, kc, vc, sm)
-    out = pkv.prefill_attention_varlen(w.q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
-                                       meta["max_seqlen_q"], meta["max_seqlen_k"], w.scale,
-                                       k=w.k_new, v=w.v_new)
+    bt = _bt(w, meta)
+    if bt is not None:
+        out = pkv.prefill_attention_varlen(w.q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                           meta["max_seqlen_q"], meta["max_seqlen_k"], w.scale,
+                                           k_cache=kc, v_cache=vc, block_tables=bt)
+    else:
+        out = pkv.prefill_attention_varlen(w.q, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                           meta["max_seqlen_q"], meta["max_seqlen_k"], w.scale,
+                                           k=w.k_new, v=w.v_new)
     torch.cuda.synchronize()
     return out, kc, vc
 
@@ -68,11 +86,13 @@ def _check_against_oracle_and_separate(w):
     want, kp, vp, _ = oracle.run_workload(w)
     assert np.array_equal(raw(kc), raw(kp)), "k pool differs from the oracle's"
     assert np.array_equal(raw(vc), raw(vp)), "v pool differs from the oracle's"
+    del kp, vp
     err = max_abs_err(out, want)
     say(f"  max |err| = {err:.3e}")
     assert err <= TOL[w.dtype]
+    del want
     out2, kc2, vc2 = _separate(wd)
-    assert torch.equal(out, out2), "fused output differs from store + prefill"
+    assert torch.equal(raw_t(out), raw_t(out2)), "fused output differs from store + prefill"
     assert torch.equal(raw_t(kc), raw_t(kc2)) and torch.equal(raw_t(vc), raw_t(vc2))
 
 
@@ -80,12 +100,12 @@ def raw_t(x: torch.Tensor) -> torch.Tensor:
     return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
 
 
-@pytest.mark.parametrize("preset", [(3, None), (1, "prefill")], ids=["preset3", "preset1-fp32"])
+@pytest.mark.parametrize("preset", [(3, None), (1, "prefill"), (4, None), (6, None), (7, None)],
+                         ids=["preset3", "preset1-fp32", "preset4-prefix", "preset6-decode-rows",
+                              "preset7-mixed"])
 def test_fused_store_presets(cuda, preset):
     say(f"[gpu] fused store + prefill, preset {preset}")
-    w = make_workload(*preset)
-    assert not w.use_block_tables and all(c == 0 for c in w.num_cached)
-    _check_against_oracle_and_separate(w)
+    _check_against_oracle_and_separate(make_workload(*preset))
 
 
 CASES = [
@@ -98,6 +118,51 @@ CASES = [
     ([1, 2, 3, 31, 32, 33, 63, 64, 65], 32, 4, 32),   # lengths around the wave and tile sizes, group 8
     ([2048, 17], 16, 8, 64),                   # a long prompt beside a short one
 ]
+
+
+PREFIX_CASES = [
+    # (lens, cached, Hq, Hkv, bs)
+    ([200, 77, 1, 129], [64, 16, 0, 128], 8, 2, 16),      # 4-key groups; one sequence without a prefix
+    ([300, 200], [256, 128], 16, 8, 64),                  # prefixes of whole tiles, tile-sized blocks
+    ([600, 129, 70], [320, 64, 0], 8, 2, 64),             # whole-block prefixes of 5 and 1 blocks
+    ([513, 300], [256, 0], 32, 4, 128),                   # group 8
+    ([1100, 300], [1024, 100], 32, 2, 256),               # group 16, blocks of 256
+    ([90, 250, 33], [40, 0, 32], 8, 2, 32),               # prefixes ending inside a tile
+    ([150, 70], [64, 0], 8, 4, 8),                        # blocks of 8
+    ([150, 70], [64, 0], 8, 4, 2),                        # blocks of 2: the two-kernel form
+    ([17, 18, 3000], [16, 16, 2999], 4, 2, 16),           # Lq 1 and 2; a decode row over 3000 keys
+    ([4096], [2048], 4, 1, 256),                          # 2048 new rows over 4096 keys
+]
+
+
+@pytest.mark.parametrize("case", PREFIX_CASES, ids=[f"fsp{i}" for i in range(len(PREFIX_CASES))])
+def test_fused_store_prefix_hits(cuda, case):
+    lens, cached, hq, hkv, bs = case
+    say(f"[gpu] fused store + prefill with cached prefixes {case}")
+    w = custom_workload(phase="prefill", seq_lens=lens, num_cached=cached, num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=128, block_size=bs, dtype=torch.bfloat16,
+                        seed=sum(lens) + 13 * bs, use_block_tables=True)
+    _check_against_oracle_and_separate(w)
+
+
+def test_fused_store_misaligned_prefixes_on_whole_tile_blocks(cuda):
+    """Blocks of 64 and 128 keys with cached prefixes that end inside a tile
+    (prefix caching caches whole blocks, but a caller may cut anywhere): the
+    one tile that holds both kinds of key is loaded lane by lane."""
+    for lens, cached, bs in (([300, 200, 77], [100, 37, 70], 64), ([700, 260], [333, 129], 128)):
+        say(f"[gpu] fused store + prefill, prefixes {cached} over blocks of {bs}")
+        w = custom_workload(phase="prefill", seq_lens=lens, num_cached=cached, num_q_heads=8,
+                            num_kv_heads=2, head_dim=128, block_size=bs, dtype=torch.bfloat16,
+                            seed=sum(cached) + bs, use_block_tables=True)
+        _check_against_oracle_and_separate(w)
+
+
+def test_fused_store_through_the_pool_without_a_prefix(cuda):
+    say("[gpu] fused store + prefill: keys through block tables, no cached prefix")
+    w = custom_workload(phase="prefill", seq_lens=[257, 33, 130], num_cached=[0, 0, 0], num_q_heads=8,
+                        num_kv_heads=4, head_dim=128, block_size=16, dtype=torch.bfloat16, seed=21,
+                        use_block_tables=True)
+    _check_against_oracle_and_separate(w)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"fs{i}" for i in range(len(CASES))])
@@ -137,7 +202,7 @@ def test_fused_store_skips_padding_and_out_of_pool_slots(cuda):
     sm2[1::7] = num_slots + 3
     out_f, kc_f, vc_f, _ = _fused(wd, sm2)
     out_s, kc_s, vc_s = _separate(wd, sm2)
-    assert torch.equal(out_f, out_s)
+    assert torch.equal(raw_t(out_f), raw_t(out_s))
     assert torch.equal(raw_t(kc_f), raw_t(kc_s)) and torch.equal(raw_t(vc_f), raw_t(vc_s))
 
 
@@ -150,7 +215,7 @@ def test_fused_store_through_run_step(cuda):
         outs.append((run_step(step_inputs_of(w, fuse_store=fuse), w.q, w.k_new, w.v_new, kc, vc), kc, vc))
     torch.cuda.synchronize()
     (o0, k0, v0), (o1, k1, v1) = outs
-    assert torch.equal(o0, o1)
+    assert torch.equal(raw_t(o0), raw_t(o1))
     assert torch.equal(raw_t(k0), raw_t(k1)) and torch.equal(raw_t(v0), raw_t(v1))
 
 
@@ -162,6 +227,6 @@ def test_fused_store_empty_batch(cuda):
     kv = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
     cu = torch.zeros(1, dtype=torch.int32, device="cuda")
     sm = torch.zeros(0, dtype=torch.int32, device="cuda")
-    out = pkv.prefill_store_attention_varlen(q, kv, kv, kc, vc, sm, cu, 0, 0.088)
+    out = pkv.prefill_store_attention_varlen(q, kv, kv, kc, vc, sm, cu, cu, 0, 0, 0.088)
     torch.cuda.synchronize()
     assert out.shape == (0, 8, 128) and not kc.any() and not vc.any()

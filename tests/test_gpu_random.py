@@ -4,8 +4,8 @@ groups (including 3 and 6), head_dim (64, 128), dtype (bf16, fp32), block
 size (1..512) and forced partition size are drawn from fixed seeds, so that
 combinations no hand-picked edge case spans are exercised. Each case is small
 enough for the oracle; the tolerance is the attention bar (2e-2 bf16, 1e-4
-fp32) and the pools are compared bit for bit. The prefill shapes are also run
-without a cached prefix through prefill_store_attention_varlen, which must
+fp32) and the pools are compared bit for bit. The prefill shapes (with their
+cached prefixes) also go through prefill_store_attention_varlen, which must
 match the oracle and equal the separate store and attention calls bit for
 bit."""
 import numpy as np
@@ -15,7 +15,7 @@ import torch
 import oracle
 import paged_kv_cache_125_amd as pkv
 from gpu_helpers import gpu_run, max_abs_err, raw, say, to_device
-from paged_kv_cache_125_amd.step import alloc_pool
+from paged_kv_cache_125_amd.step import alloc_pool, write_ranges
 from workloads import custom_workload
 
 pytestmark = pytest.mark.gpu
@@ -92,17 +92,22 @@ def test_random_prefill(cuda, i):
 
 @pytest.mark.parametrize("i", range(N_CASES), ids=lambda i: f"fs-r{i}")
 def test_random_fused_store_prefill(cuda, i):
-    lens, _, hq, hkv, d, dt, bs = prefill_case(i)
-    say(f"[gpu] random fused store + prefill {i}: lens {lens} Hq {hq} Hkv {hkv} d {d} {dt} bs {bs}")
-    w = custom_workload(phase="prefill", seq_lens=lens, num_cached=[0] * len(lens), num_q_heads=hq,
-                        num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dt, seed=190 + i,
-                        use_block_tables=False)
+    lens, cached, hq, hkv, d, dt, bs = prefill_case(i)
+    say(f"[gpu] random fused store + prefill {i}: lens {lens} cached {cached} Hq {hq} Hkv {hkv} "
+        f"d {d} {dt} bs {bs}")
+    w = custom_workload(phase="prefill", seq_lens=lens, num_cached=cached, num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dt, seed=190 + i)
     wd = to_device(w, "cuda")
-    out, kc, vc = gpu_run(wd)   # store_kvcache, then prefill over k/v
+    out, kc, vc = gpu_run(wd)   # store_kvcache, then prefill
     kf, vf = alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype, "cuda")
+    write_ranges(w.hist, w.block_tables, w.block_size, wd.k_hist, wd.v_hist, kf, vf)
     meta = pkv.pack_prefill(w.seq_lens, w.num_cached, w.block_tables, w.block_size, device="cuda")
+    bt = meta["block_tables"]
+    if bt is None and w.use_block_tables:
+        bt = pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cuda")["block_tables"]
     of = pkv.prefill_store_attention_varlen(wd.q, wd.k_new, wd.v_new, kf, vf, meta["slot_mapping"],
-                                            meta["cu_seqlens_q"], meta["max_seqlen_q"], w.scale)
+                                            meta["cu_seqlens_q"], meta["cu_seqlens_k"], meta["max_seqlen_q"],
+                                            meta["max_seqlen_k"], w.scale, block_tables=bt)
     torch.cuda.synchronize()
     assert np.array_equal(raw(of), raw(out)), "fused output differs from the separate calls"
     assert np.array_equal(raw(kf), raw(kc)) and np.array_equal(raw(vf), raw(vc))
@@ -111,4 +116,3 @@ def test_random_fused_store_prefill(cuda, i):
     err = max_abs_err(of, want)
     say(f"  max |err| = {err:.3e}")
     assert err <= TOL[dt]
-
