@@ -189,7 +189,7 @@ size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q, int32
  *    The two forms agree when slot_mapping[cu_seqlens_q[s] + i] is the slot
  *    of that position under sequence s's block table.
  *
- * For bf16 and head_dim 128 (block_size >= 4 with block tables) this is one
+ * For bf16 and head_dim 128 (block_size >= 16 with block tables) this is one
  * launch: after its attention, each query block copies its own rows of k/v
  * into their slots (the group's query heads share the copy; the rows were
  * read for the block's last key tiles moments before). Other shapes run the

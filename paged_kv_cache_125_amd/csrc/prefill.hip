@@ -61,7 +61,8 @@ __device__ __forceinline__ int64_t prefill_key_off(const PrefillArgs &a, int s, 
 enum KeySource {
     kContiguous = 0,   // the call's k/v rows: one descriptor per tile
     kPoolBlocks = 1,   // the pool, block_size a multiple of 64: one descriptor per tile
-    kPoolSmall = 2     // the pool, block_size 4..32: one descriptor per 4 keys
+    kPoolSmall = 2,    // the pool, block_size 4 or 8: one descriptor per 4 keys
+    kPoolWave = 3      // the pool, block_size 16 or 32: one descriptor per wave's 16 keys
 };
 
 // LDS tile layout: 64 keys x 256 bytes, no padding; the 16-byte chunk c of key
@@ -93,7 +94,8 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __attribute__
 // ones this call stores -- are read from those rows rather than the pool.
 template <int SRC, int NW, int RB, int WPE, bool PERSIST, bool STORE>
 __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
-    static_assert(!STORE || (RB == 1 && !PERSIST), "the fused store is built for the fixed grid");
+    static_assert(!STORE || (RB == 1 && !PERSIST && SRC != kPoolSmall),
+                  "the fused store is built for the fixed grid and tiles of whole 16-key slices");
     constexpr int BM = 32 * RB * NW;         // query rows per workgroup (one query head)
     constexpr int LPW = 16 / NW;   // 1 KiB direct-load instructions per wave per K (or V) tile
     static_assert(NW * LPW == 16 && NW >= 2, "waves must split a tile evenly");
@@ -153,7 +155,10 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
     typedef const __attribute__((address_space(4))) int32_t *bt_ptr;
     const bt_ptr bt_row = (bt_ptr)(a.bt + (int64_t)s * a.maxb);
     constexpr int NB = SRC == kPoolSmall ? LPW : 1;   // block ids per wave and tile
-    auto key_of = [&](int k0, int i) { return SRC == kPoolSmall ? k0 + 4 * (LPW * wave + i) : k0; };
+    // first key of block-id slot i of the wave in tile k0
+    auto key_of = [&](int k0, int i) {
+        return SRC == kPoolSmall ? k0 + 4 * (LPW * wave + i) : SRC == kPoolWave ? k0 + 4 * LPW * wave : k0;
+    };
     // All four bounds in one round trip (a workgroup with no rows here
     // learns it from the first two and leaves).
     const int q_start = a.cu_q[s], q_end = a.cu_q[s + 1];
@@ -247,8 +252,9 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
     for (int i = 0; i < LPW; ++i) {
         const int t = 4 * (LPW * wave + i) + (lane >> 4);
         const int chunk = (lane & 15) ^ tile_swz(t);
-        voff[i] = SRC == kPoolSmall ? (lane >> 4) * (int)stride_b + 16 * chunk
-                                    : t * (int)stride_b + 16 * chunk - 1024 * i;
+        voff[i] = SRC == kPoolSmall  ? (lane >> 4) * (int)stride_b + 16 * chunk
+                  : SRC == kPoolWave ? (t - 4 * LPW * wave) * (int)stride_b + 16 * chunk - 1024 * i
+                                     : t * (int)stride_b + 16 * chunk - 1024 * i;
     }
     typedef __attribute__((address_space(3))) void lds_t;
     // Fused store over the pool: keys at positions off and beyond come from
@@ -264,8 +270,7 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
         for (int i = 0; i < LPW; ++i) {
             const int t = 4 * (LPW * wave + i) + (lane >> 4);
             const int chunk = (lane & 15) ^ tile_swz(t);
-            voff_n[i] = SRC == kPoolSmall ? (lane >> 4) * (int)stride_n + 16 * chunk
-                                          : t * (int)stride_n + 16 * chunk - 1024 * i;
+            voff_n[i] = t * (int)stride_n + 16 * chunk - 1024 * i;
         }
     }
     // Descriptor over the call's rows from key `key0` on (the base may lie
@@ -283,45 +288,30 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
             if (k0 >= off) {
                 // every key of the tile is this call's: its rows, as in the contiguous form
                 const int nkeys = min(kPfBN, kend - k0);
-                if constexpr (SRC == kPoolSmall) {
-#pragma unroll
-                    for (int i = 0; i < LPW; ++i) {
-                        const int key0 = k0 + 4 * (LPW * wave + i);
-                        const int nk = min(4, kend - key0);
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(knbase, key0, nk), (lds_t *)(kd + 1024 * i), 16, voff_n[i], 0, 0, 0);
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(vnbase, key0, nk), (lds_t *)(vd + 1024 * i), 16, voff_n[i], 0, 0, 0);
-                    }
-                } else {
-                    dma_tile(rows_rsrc(knbase, k0, nkeys), (lds_t *)kd, voff_n, std::make_integer_sequence<int, LPW>{});
-                    dma_tile(rows_rsrc(vnbase, k0, nkeys), (lds_t *)vd, voff_n, std::make_integer_sequence<int, LPW>{});
-                }
+                dma_tile(rows_rsrc(knbase, k0, nkeys), (lds_t *)kd, voff_n, std::make_integer_sequence<int, LPW>{});
+                dma_tile(rows_rsrc(vnbase, k0, nkeys), (lds_t *)vd, voff_n, std::make_integer_sequence<int, LPW>{});
                 return;
             }
             if (k0 + kPfBN > off) {
                 // The tile holds both (at most one such tile per item): each
                 // load goes out twice with complementary lane masks, cached
-                // keys from the pool and the rest from the rows. Masked-off
-                // lanes neither read nor write LDS.
+                // keys from the pool and the rest from the rows, each at its
+                // own LDS base. Masked-off lanes neither read nor write LDS.
                 const int nkeys = min(kPfBN, kend - k0);
 #pragma unroll
                 for (int i = 0; i < LPW; ++i) {
                     const int t = 4 * (LPW * wave + i) + (lane >> 4);
                     const int chunk = (lane & 15) ^ tile_swz(t);
                     const int key0 = k0 + 4 * (LPW * wave + i);
-                    int blk, prow, np;   // the cached keys' block, pool row of the base, keys in range
-                    if constexpr (SRC == kPoolSmall) {
-                        blk = pre_blk[i];
-                        prow = key0 & (a.bs - 1);
-                        np = min(4, off - key0);
-                    } else {
-                        blk = pre_blk[0];
-                        prow = k0 & (a.bs - 1);
-                        np = off - k0;
-                    }
+                    // the cached keys' descriptor: its first key (the tile's, or the
+                    // wave's slice's), block, and keys in range
+                    const int pk = key_of(k0, 0);
+                    const int blk = pre_blk[0];
+                    const int np = min(SRC == kPoolWave ? 4 * LPW : kPfBN, off - pk);
                     const bool ok = (uint32_t)blk < (uint32_t)a.num_blocks;
                     const int nrec = __builtin_amdgcn_readfirstlane(ok ? max(0, np) * (int)stride_b : 0);
-                    const int64_t rb_ = ((int64_t)(ok ? blk : 0) * a.bs + prow) * stride_b;
-                    const int vo_p = (SRC == kPoolSmall ? (lane >> 4) : t) * (int)stride_b + 16 * chunk;
+                    const int64_t rb_ = ((int64_t)(ok ? blk : 0) * a.bs + (pk & (a.bs - 1))) * stride_b;
+                    const int vo_p = (k0 + t - pk) * (int)stride_b + 16 * chunk;
                     const int vo_n = t * (int)stride_n + 16 * chunk;
                     if (k0 + t < off) {
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -352,15 +342,17 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_t *)(vd + 1024 * i), 16, voff[i], 0, 0, 0);
             }
         } else {
-            const int nkeys = min(kPfBN, max(0, kend - k0));
-            int64_t row0;   // first key row of the tile in its source
+            // kPoolWave: the same with the wave's 16 keys (one block) as the tile
+            const int kw0 = key_of(k0, 0);
+            const int nkeys = min(SRC == kPoolWave ? 4 * LPW : kPfBN, max(0, kend - kw0));
+            int64_t row0;   // first key row of the tile (or the wave's slice) in its source
             bool ok = true;
             if constexpr (SRC == kContiguous) {
                 row0 = (int64_t)k_start + k0;
             } else {
                 const int blk = pre_blk[0];
                 ok = (uint32_t)blk < (uint32_t)a.num_blocks;
-                row0 = (int64_t)(ok ? blk : 0) * a.bs + (k0 & (a.bs - 1));
+                row0 = (int64_t)(ok ? blk : 0) * a.bs + (kw0 & (a.bs - 1));
             }
             const int nrec = __builtin_amdgcn_readfirstlane(ok ? nkeys * (int)stride_b : 0);
             const int64_t rb_ = row0 * stride_b;
@@ -925,6 +917,23 @@ static int prefill_cus() {
     return cached[dev];
 }
 
+// The fused store's copy as a store_kvcache launch (for the shapes that run
+// it as a kernel of its own).
+static hipError_t launch_store_of(const PrefillArgs &a, int dtype, hipStream_t stream) {
+    const int es = dtype == 1 ? 2 : 4;
+    StoreArgs sa;
+    sa.k = (const uint8_t *)a.k;
+    sa.v = (const uint8_t *)a.v;
+    sa.k_stride_bytes = sa.v_stride_bytes = a.kv_stride * es;
+    sa.kc = (uint8_t *)a.store_kc;
+    sa.vc = (uint8_t *)a.store_vc;
+    sa.slots = a.slots;
+    sa.num_tokens = a.total_q;
+    sa.chunks_per_row = a.Hkv * a.d * es / 16;
+    sa.num_slots = a.num_slots;
+    return launch_store(sa, stream);
+}
+
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
     if (a.num_seqs == 0 || a.max_seqlen_q == 0) return hipSuccess;
     // The MFMA kernel's direct tile loads address up to 64 key rows per
@@ -958,17 +967,26 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
             hipLaunchKernelGGL((prefill_mfma_kernel<kContiguous, NW, RB, 2, P>), grid, block, 0, stream, a); \
         else if (a.bs % kPfBN == 0)                                                                       \
             hipLaunchKernelGGL((prefill_mfma_kernel<kPoolBlocks, NW, RB, 2, P>), grid, block, 0, stream, a); \
+        else if (a.bs >= 4 * (16 / NW))                                                                   \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolWave, NW, RB, 2, P>), grid, block, 0, stream, a);   \
         else                                                                                              \
             hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2, P>), grid, block, 0, stream, a);  \
     } while (0)
-        if (a.slots) {
+        if (a.slots && (!a.paged || a.bs >= 4 * (16 / NW))) {
             const dim3 g((unsigned)nwg_fixed);
             if (!a.paged)
                 hipLaunchKernelGGL((prefill_store_mfma_kernel<kContiguous, NW, 2>), g, block, 0, stream, a);
             else if (a.bs % kPfBN == 0)
                 hipLaunchKernelGGL((prefill_store_mfma_kernel<kPoolBlocks, NW, 2>), g, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((prefill_store_mfma_kernel<kPoolSmall, NW, 2>), g, block, 0, stream, a);
+                hipLaunchKernelGGL((prefill_store_mfma_kernel<kPoolWave, NW, 2>), g, block, 0, stream, a);
+        } else if (a.slots) {
+            // Blocks of 4 or 8 keys: the store kernel, then attention. (The
+            // fused form of the per-4-key loads ran out of scalar registers
+            // and was slower than the two launches.)
+            const hipError_t e = launch_store_of(a, dtype, stream);
+            if (e != hipSuccess) return e;
+            PKV_MFMA_LAUNCH(false);
         } else if (persist) {
             PKV_MFMA_LAUNCH(true);
         } else {
@@ -979,18 +997,7 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
         if (a.slots) {
             // Other dtypes, head sizes and block sizes: the store kernel, then
             // attention (over the pool when there are block tables).
-            const int es = dtype == 1 ? 2 : 4;
-            StoreArgs sa;
-            sa.k = (const uint8_t *)a.k;
-            sa.v = (const uint8_t *)a.v;
-            sa.k_stride_bytes = sa.v_stride_bytes = a.kv_stride * es;
-            sa.kc = (uint8_t *)a.store_kc;
-            sa.vc = (uint8_t *)a.store_vc;
-            sa.slots = a.slots;
-            sa.num_tokens = a.total_q;
-            sa.chunks_per_row = a.Hkv * a.d * es / 16;
-            sa.num_slots = a.num_slots;
-            const hipError_t e = launch_store(sa, stream);
+            const hipError_t e = launch_store_of(a, dtype, stream);
             if (e != hipSuccess) return e;
         }
         const dim3 grid((a.max_seqlen_q + 3) / 4, a.Hq, a.num_seqs);
