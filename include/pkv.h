@@ -236,8 +236,11 @@ int pkv_prefill_store_attention_varlen(const void *q, int64_t q_token_stride, co
  * (nano-vLLM's 256 included) the (sequence, kv head, 64-position chunk) work
  * list is divided evenly over all waves the GPU holds at once, each wave
  * finishing the sequences it covers entirely and leaving at most two partial
- * results; otherwise fixed partitions are used. A positive multiple of 16
- * forces fixed partitions of that many positions. The workspace must hold
+ * results -- except for batches of at most 64 (sequence, kv head) pairs,
+ * where fixed partitions of 64 to 512 positions are faster; other shapes use
+ * fixed partitions. PKV_PARTITION_BALANCED forces the balanced split where
+ * the shape allows it (the library's choice elsewhere). A positive multiple
+ * of 16 forces fixed partitions of that many positions. The workspace must hold
  * pkv_decode_workspace_bytes(...) bytes (256-byte aligned), and may be NULL
  * when that is 0. pkv_decode_partition_size() reports the fixed partition
  * size, or 0 for the balanced split.
@@ -252,6 +255,8 @@ int pkv_prefill_store_attention_varlen(const void *q, int64_t q_token_stride, co
  *                  context is cut to its first max_context_len positions.
  * Requires num_q_heads % num_kv_heads == 0, head_dim in {64, 128}, a positive
  * finite scale, and block_size a power of two in [1, 1024]. */
+#define PKV_PARTITION_BALANCED (-1)
+
 int pkv_decode_attention_paged(const void *q, int64_t q_token_stride, const void *k_cache,
                                const void *v_cache, const int32_t *block_tables,
                                int32_t max_blocks_per_seq, const int32_t *context_lens,

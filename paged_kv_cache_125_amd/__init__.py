@@ -31,6 +31,8 @@ LIB_PATH = os.path.join(_PKG, "libpkv.so")
 ABI_VERSION = 5
 
 PKV_F32, PKV_BF16 = 0, 1
+# partition_size for decode_attention_paged: force the balanced split where the shape allows it
+PARTITION_BALANCED = -1
 _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_ELAUNCH", 4: "PKV_ENOSPACE"}
 
 EXPORTED = [

@@ -400,8 +400,8 @@ int decode_call(const char *fn, const void *q, int64_t q_token_stride, const voi
     int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs, scale);
     if (rc) return rc;
     if (max_context_len < 0) return fail(PKV_EINVAL, "%s: negative max_context_len", fn);
-    if (partition_size < 0 || partition_size % 16)
-        return fail(PKV_EINVAL, "%s: partition_size must be 0 or a positive multiple of 16", fn);
+    if ((partition_size < 0 && partition_size != PKV_PARTITION_BALANCED) || (partition_size > 0 && partition_size % 16))
+        return fail(PKV_EINVAL, "%s: partition_size must be 0, PKV_PARTITION_BALANCED or a positive multiple of 16", fn);
     if (num_seqs == 0) return PKV_OK;
     if (!q || !out || !context_lens) return fail(PKV_EINVAL, "%s: null pointer", fn);
     rc = check_pool(fn, k_cache, v_cache, block_tables, max_blocks_per_seq, num_blocks, block_size);

@@ -200,6 +200,28 @@ def test_decode_workspace_and_partition():
     assert pkv.decode_partition_size(4, 100, 4, 2, 64, 16, torch.float32, 48) == 48
 
 
+def test_small_batch_decode_takes_fixed_partitions():
+    bf = torch.bfloat16
+    # up to 64 (sequence, kv head) pairs: the shortest partition of 64..512
+    # positions with pairs * partitions <= 1024
+    assert pkv.decode_partition_size(1, 2680, 16, 8, 128, 256, bf) == 64     # 8 x 42
+    assert pkv.decode_partition_size(2, 4096, 16, 8, 128, 256, bf) == 64     # 16 x 64
+    assert pkv.decode_partition_size(4, 3296, 16, 8, 128, 256, bf) == 128    # 32 x 26
+    assert pkv.decode_partition_size(8, 3719, 16, 8, 128, 256, bf) == 256    # 64 x 15
+    assert pkv.decode_partition_size(2, 23395, 32, 8, 128, 256, bf) == 512   # capped at 512
+    # more pairs, or partials past 8 MiB: the balanced split
+    assert pkv.decode_partition_size(9, 4096, 16, 8, 128, 256, bf) == 0
+    assert pkv.decode_partition_size(64, 4096, 16, 8, 128, 256, bf) == 0
+    assert pkv.decode_partition_size(8, 1 << 20, 32, 8, 128, 256, bf) == 0
+    # forced either way
+    assert pkv.decode_partition_size(1, 2680, 16, 8, 128, 256, bf, pkv.PARTITION_BALANCED) == 0
+    assert pkv.decode_partition_size(1, 2680, 16, 8, 128, 256, bf, 128) == 128
+    # the workspace query follows the plan
+    assert pkv.decode_workspace_bytes(1, 2680, 16, 8, 128, 256, bf) >= 42 * 16 * 130 * 4
+    # where the split cannot run, BALANCED falls back to the library's partitions
+    assert pkv.decode_partition_size(4, 100, 4, 2, 64, 16, torch.float32, pkv.PARTITION_BALANCED) > 0
+
+
 def test_balanced_decode_split_only_while_its_chunk_count_fits_32_bits():
     # the balanced split counts num_seqs * Hkv * ceil(max_context_len / 64) chunks in
     # 32-bit integers; past that the plan falls back to fixed partitions, and the

@@ -136,7 +136,8 @@ def test_binding_allocations_survive_work_on_another_stream(cuda):
         del junk, got
 
 
-@pytest.mark.parametrize("partition", [0, 64, 512], ids=["balanced", "fixed-5-parts", "fixed-1-part"])
+@pytest.mark.parametrize("partition", [-1, 0, 64, 512],
+                         ids=["balanced", "library-choice", "fixed-5-parts", "fixed-1-part"])
 def test_decode_cuts_contexts_past_max_context_len(cuda, partition):
     say(f"[gpu] decode: context_lens past max_context_len are cut to it (partition {partition})")
     bs, hq, hkv, d = 64, 8, 4, 128

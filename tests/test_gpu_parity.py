@@ -260,7 +260,7 @@ def test_balanced_decode_any_wave_count(cuda, waves, monkeypatch):
     lens = [1, 64, 65, 700, 129, 2000, 63, 257]
     w = custom_workload(phase="decode", seq_lens=lens, num_cached=[n - 1 for n in lens],
                         num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=256, seed=waves)
-    out, kc, vc = gpu_run(to_device(w, "cuda"))
+    out, kc, vc = gpu_run(to_device(w, "cuda"), partition_size=pkv.PARTITION_BALANCED)
     want, *_ = oracle.run_workload(w)
     err = max_abs_err(out, want)
     say(f"  max |err| = {err:.3e}")
@@ -282,12 +282,14 @@ def test_decode_workspace_reuse(cuda):
         write_ranges(w.hist, w.block_tables, 256, wd.k_hist, wd.v_hist, kc, vc)
         meta = pkv.pack_decode(w.seq_lens, w.block_tables, 256)
         pkv.store_kvcache(wd.k_new, wd.v_new, kc, vc, meta["slot_mapping"])
+        want, *_ = oracle.run_workload(w)
         for rep in range(2):
-            out = pkv.decode_attention_paged(wd.q, kc, vc, meta["block_tables"], meta["context_lens"],
-                                             meta["max_seqlen_k"], w.scale, workspace=ws)
-            torch.cuda.synchronize()
-            want, *_ = oracle.run_workload(w)
-            assert max_abs_err(out, want) <= 2e-2
+            for part in (0, pkv.PARTITION_BALANCED):
+                out = pkv.decode_attention_paged(wd.q, kc, vc, meta["block_tables"], meta["context_lens"],
+                                                 meta["max_seqlen_k"], w.scale, workspace=ws,
+                                                 partition_size=part)
+                torch.cuda.synchronize()
+                assert max_abs_err(out, want) <= 2e-2
 
 
 def test_balanced_decode_padded_rows(cuda):
@@ -304,11 +306,30 @@ def test_balanced_decode_padded_rows(cuda):
     bt3 = torch.cat([bt[:1], pad_bt, bt[1:], pad_bt])
     ctx = torch.tensor([300, 0, 1000, 0], dtype=torch.int32, device="cuda")
     q = torch.cat([wd.q[:1], torch.ones_like(wd.q[:1]), wd.q[1:], torch.ones_like(wd.q[:1])])
-    out = pkv.decode_attention_paged(q, kc, vc, bt3, ctx, 1000, w.scale)
-    torch.cuda.synchronize()
     want, *_ = oracle.run_workload(w)
-    assert max_abs_err(out[[0, 2]], want) <= 2e-2
-    assert torch.count_nonzero(out[[1, 3]].float()) == 0
+    for part in (pkv.PARTITION_BALANCED, 0):   # the split, and the small-batch partitions
+        out = pkv.decode_attention_paged(q, kc, vc, bt3, ctx, 1000, w.scale, partition_size=part)
+        torch.cuda.synchronize()
+        assert max_abs_err(out[[0, 2]], want) <= 2e-2
+        assert torch.count_nonzero(out[[1, 3]].float()) == 0
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 9])
+def test_small_batch_decode_plan(cuda, B):
+    # Up to 64 (sequence, kv head) pairs the library takes fixed partitions
+    # (64..512 positions); both plans must match the oracle on the same batch.
+    from workloads import restrict
+    w = restrict(make_workload(2), list(range(B)))
+    P = pkv.decode_partition_size(B, max(w.seq_lens), w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                  w.block_size, w.dtype)
+    say(f"[gpu] small-batch decode, B {B}: plan partition {P}")
+    assert (P in (64, 128, 256, 512)) if B * w.num_kv_heads <= 64 else P == 0
+    want, *_ = oracle.run_workload(w)
+    for part in (0, pkv.PARTITION_BALANCED):
+        out, *_ = gpu_run(to_device(w, "cuda"), partition_size=part)
+        err = max_abs_err(out, want)
+        say(f"  partition_size {part}: max |err| = {err:.3e}")
+        assert err <= 2e-2
 
 
 MIXED = [

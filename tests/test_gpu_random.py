@@ -40,7 +40,7 @@ def decode_case(i):
     hkv, hq, d, dt, bs = _shape(rng)
     b = int(rng.integers(1, 13))
     lens = [int(x) for x in rng.integers(1, 3001, b)]
-    part = int(rng.choice([0, 0, 16, 64, 128]))
+    part = int(rng.choice([0, -1, 16, 64, 128]))   # -1: the balanced split, forced
     return lens, hq, hkv, d, dt, bs, part
 
 
