@@ -204,54 +204,62 @@ def _token_stride(t: torch.Tensor) -> int:
 _ATTN_DTYPES = (torch.bfloat16, torch.float32)
 
 
-def _need(cond: bool, msg: str) -> None:
+def _need(cond: bool, msg) -> None:
+    """Raise ValueError(msg) unless cond; msg may be a callable that formats
+    the message, so that a passing check formats nothing."""
     if not cond:
-        raise ValueError(msg)
+        raise ValueError(msg() if callable(msg) else msg)
 
 
 def _one_gpu(**tensors) -> None:
     """All given tensors on one device, and that device a GPU."""
-    devs = {name: t.device for name, t in tensors.items() if t is not None}
-    _need(len(set(devs.values())) == 1,
-          "tensors on different devices: " + ", ".join(f"{n} on {d}" for n, d in devs.items()))
-    _need(next(iter(devs.values())).type == "cuda", "the tensors must be on a GPU")
+    dev = None
+    for t in tensors.values():
+        if t is None:
+            continue
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices: " + ", ".join(
+                f"{n} on {x.device}" for n, x in tensors.items() if x is not None))
+    _need(dev is not None and dev.type == "cuda", "the tensors must be on a GPU")
 
 
 def _int32_vec(t: torch.Tensor, name: str, min_len: int) -> None:
-    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}")
-    _need(t.dim() == 1 and t.is_contiguous(), f"{name} must be a contiguous 1-D tensor")
-    _need(t.numel() >= min_len, f"{name} has {t.numel()} entries, needs {min_len}")
+    _need(t.dtype == torch.int32, lambda: f"{name} must be int32, got {t.dtype}")
+    _need(t.dim() == 1 and t.is_contiguous(), lambda: f"{name} must be a contiguous 1-D tensor")
+    _need(t.numel() >= min_len, lambda: f"{name} has {t.numel()} entries, needs {min_len}")
 
 
 def _int32_table(t: torch.Tensor, name: str, min_rows: int) -> None:
-    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}")
-    _need(t.dim() == 2 and t.is_contiguous(), f"{name} must be a contiguous 2-D tensor")
+    _need(t.dtype == torch.int32, lambda: f"{name} must be int32, got {t.dtype}")
+    _need(t.dim() == 2 and t.is_contiguous(), lambda: f"{name} must be a contiguous 2-D tensor")
     _need(t.shape[0] >= min_rows and t.shape[1] >= 1,
-          f"{name} has shape {tuple(t.shape)}, needs at least {min_rows} rows")
+          lambda: f"{name} has shape {tuple(t.shape)}, needs at least {min_rows} rows")
 
 
 def _pool(k_cache: torch.Tensor, v_cache: torch.Tensor, dtype: torch.dtype) -> None:
     _need(k_cache.dim() == 4, "caches must be [num_blocks, block_size, num_kv_heads, head_dim]")
     _need(k_cache.shape == v_cache.shape, "k_cache and v_cache differ in shape")
     _need(k_cache.dtype == dtype and v_cache.dtype == dtype,
-          f"cache dtype {k_cache.dtype}/{v_cache.dtype} differs from {dtype}")
+          lambda: f"cache dtype {k_cache.dtype}/{v_cache.dtype} differs from {dtype}")
     _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
 
 
 def _rows(t: torch.Tensor, name: str, heads: int, head_dim: int, dtype: torch.dtype,
           min_rows: int) -> None:
     """[tokens, heads, head_dim] with contiguous rows, of the given dtype."""
-    _need(t.dtype == dtype, f"{name} dtype {t.dtype} differs from {dtype}")
+    _need(t.dtype == dtype, lambda: f"{name} dtype {t.dtype} differs from {dtype}")
     _need(t.dim() == 3 and t.shape[1] == heads and t.shape[2] == head_dim,
-          f"{name} has shape {tuple(t.shape)}, expected [tokens, {heads}, {head_dim}]")
-    _need(t.shape[0] >= min_rows, f"{name} has {t.shape[0]} rows, needs {min_rows}")
+          lambda: f"{name} has shape {tuple(t.shape)}, expected [tokens, {heads}, {head_dim}]")
+    _need(t.shape[0] >= min_rows, lambda: f"{name} has {t.shape[0]} rows, needs {min_rows}")
     _token_stride(t)
 
 
 def _out(out: torch.Tensor, like: torch.Tensor) -> None:
-    _need(out.dtype == like.dtype, f"out dtype {out.dtype} differs from q's {like.dtype}")
+    _need(out.dtype == like.dtype, lambda: f"out dtype {out.dtype} differs from q's {like.dtype}")
     _need(tuple(out.shape) == tuple(like.shape),
-          f"out has shape {tuple(out.shape)}, expected {tuple(like.shape)}")
+          lambda: f"out has shape {tuple(out.shape)}, expected {tuple(like.shape)}")
     _need(out.is_contiguous(), "out must be contiguous")
 
 
@@ -422,7 +430,7 @@ def prefill_attention_varlen(q: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seq
     when allocated and left zeroed by every call) selects the persistent grid
     and must not be shared by calls that may overlap."""
     _need(q.dim() == 3, "q must be [tokens, num_q_heads, head_dim]")
-    _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
+    _need(q.dtype in _ATTN_DTYPES, lambda: f"unsupported dtype {q.dtype}")
     total_q, hq, d = q.shape
     _rows(q, "q", hq, d, q.dtype, 0)
     _int32_vec(cu_seqlens_q, "cu_seqlens_q", 1)
@@ -482,7 +490,7 @@ def prefill_store_attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Te
     k/v rows; with them, cached positions come from the pool and this call's
     positions from its k/v rows."""
     _need(q.dim() == 3, "q must be [tokens, num_q_heads, head_dim]")
-    _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
+    _need(q.dtype in _ATTN_DTYPES, lambda: f"unsupported dtype {q.dtype}")
     total_q, hq, d = q.shape
     _rows(q, "q", hq, d, q.dtype, 0)
     _pool(k_cache, v_cache, q.dtype)
@@ -542,7 +550,7 @@ def decode_attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     sequence. ``workspace`` (uint8, >= decode_workspace_bytes) is allocated
     through torch when not given."""
     _need(q.dim() == 3, "q must be [num_seqs, num_q_heads, head_dim]")
-    _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
+    _need(q.dtype in _ATTN_DTYPES, lambda: f"unsupported dtype {q.dtype}")
     B, hq, d = q.shape
     _rows(q, "q", hq, d, q.dtype, 0)
     _pool(k_cache, v_cache, q.dtype)
@@ -583,7 +591,7 @@ def decode_attention_paged_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cac
     allocate. ``out`` must be given; nothing is allocated on the path. Calls
     that may overlap on one GPU race on its scratch."""
     _need(q.dim() == 3, "q must be [num_seqs, num_q_heads, head_dim]")
-    _need(q.dtype in _ATTN_DTYPES, f"unsupported dtype {q.dtype}")
+    _need(q.dtype in _ATTN_DTYPES, lambda: f"unsupported dtype {q.dtype}")
     B, hq, d = q.shape
     _rows(q, "q", hq, d, q.dtype, 0)
     _pool(k_cache, v_cache, q.dtype)
