@@ -37,6 +37,7 @@ import argparse
 import gc
 import hashlib
 import json
+import math
 import os
 import platform
 import sys
@@ -528,10 +529,13 @@ STREAM_BYTES = 2 << 30          # buffer of the read-only streaming reference
 def stream_read_rates(reps: int = 5) -> dict:
     """GB/s of libpkv_probe's read-only streaming kernels over a 2 GiB buffer
     of random words (8x the last-level cache, so every pass comes from HBM),
-    timed with events on the current stream: the plain grid-stride form and the
-    decode-shaped form (2 KB rows of eight 256-byte heads, one head per wave),
-    each at 4, 8 and 16 workgroups per CU, the best kept. An achievable
-    streaming-read reference beside the published 8 TB/s."""
+    timed with events on the current stream: the plain grid-stride form, the
+    decode-shaped form (2 KB rows of eight 256-byte heads, one head per wave)
+    and one contiguous span per wave, each at 1, 2, 3, 4, 6, 8 and 16
+    workgroups per CU (the rate is not monotonic in the count: the grid-stride
+    form reads addresses a grid apart, and some grid sizes land them on few
+    channels), the best of each kept. An achievable streaming-read reference
+    beside the published 8 TB/s."""
     import ctypes
     from paged_kv_cache_125_amd.build import PROBE_LIB
     L = ctypes.CDLL(PROBE_LIB)
@@ -547,9 +551,9 @@ def stream_read_rates(reps: int = 5) -> dict:
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     out = {}
-    for mode, name in ((0, "plain"), (1, "decode_shaped")):
+    for mode, name in ((0, "plain"), (1, "decode_shaped"), (2, "span")):
         best = None
-        for per_cu in (4, 8, 16):
+        for per_cu in (1, 2, 3, 4, 6, 8, 16):
             blocks = cus * per_cu
             args = (ctypes.c_void_p(buf.data_ptr()), STREAM_BYTES, mode, 2048, blocks,
                     ctypes.c_void_p(sink.data_ptr()), stream)
@@ -566,6 +570,7 @@ def stream_read_rates(reps: int = 5) -> dict:
         out[name] = best
     del buf
     torch.cuda.empty_cache()
+    out["best"] = max((out[n] for n in ("plain", "decode_shaped", "span")), key=lambda r: r["GBps"])
     out["bytes_read"] = STREAM_BYTES
     return out
 
@@ -802,13 +807,15 @@ TRACE_KERNELS = {"decode": ["decode_sk_kernel", "decode_sk_reduce_kernel"],
                  "prefill": ["prefill_mfma_kernel"]}
 
 
-def summarize_trace(trace_dir, workload, steps, warmup, command):
+def summarize_trace(trace_dir, workload, steps, warmup, command, settle=None):
     """Per-workload kernel durations from a `rocprofv3 --kernel-trace` run of
     `bench.py --workload W --steps K --warmup W'`. The bench runs every pass
     (warmup, wall-clock, event-timed) part by part, so the n-th dispatch of an
     attention kernel belongs to a known part; that order is rebuilt here and
     checked against the dispatch count. Durations of the two timed passes only
-    (warmup excluded). Prints a markdown summary."""
+    (warmup and the event pass's settle steps excluded); `settle` is the run's
+    settle steps per chunk, by part, as its bench line reports them. Prints a
+    markdown summary."""
     import csv
     import glob
     rows = []
@@ -828,8 +835,14 @@ def summarize_trace(trace_dir, workload, steps, warmup, command):
         mine = [p for p in parts if p[0] == phase]
         if not mine:
             continue
-        order = [(p, pas) for pas, n in (("warmup", warmup), ("timed", steps), ("events", steps))
-                 for p in mine for _ in range(n)]
+        settle_of = dict(zip(parts, settle or [0] * len(parts)))
+        # the warmup pass ends with the three steps that time a part's step
+        n_warm = warmup + min(3, warmup + steps)
+        order = [(p, pas) for pas, n in (("warmup", n_warm), ("timed", steps)) for p in mine for _ in range(n)]
+        for p in mine:
+            for c0 in range(0, steps, EVENT_CHUNK_STEPS):
+                order += [(p, "settle")] * settle_of[p]
+                order += [(p, "events")] * (min(c0 + EVENT_CHUNK_STEPS, steps) - c0)
         for k in kernels:
             durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
                     for r in rows if r["Kernel_Name"].split("(")[0].split("<")[0].endswith(k)]
@@ -838,7 +851,7 @@ def summarize_trace(trace_dir, workload, steps, warmup, command):
             if len(durs) != len(order):
                 raise SystemExit(f"{k}: {len(durs)} dispatches, expected {len(order)}")
             for p in mine:
-                d = [t for t, (pp, pas) in zip(durs, order) if pp == p and pas != "warmup"]
+                d = [t for t, (pp, pas) in zip(durs, order) if pp == p and pas in ("timed", "events")]
                 out.append(f"| {k} | {names.get(p[1], p[1])} (preset {p[1]}) | {len(d)} | "
                            f"{np.mean(d):.1f} | {np.median(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
             if k == kernels[0]:
@@ -852,7 +865,7 @@ def summarize_trace(trace_dir, workload, steps, warmup, command):
     per = {}
     for t0, p, pas in sorted(first, key=lambda x: x[0]):
         i = int(np.searchsorted(starts, t0)) - 1
-        if i >= 0 and pas != "warmup":
+        if i >= 0 and pas in ("timed", "events"):
             r = stores[i]
             per.setdefault(p, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
     for p in parts:
@@ -867,6 +880,15 @@ def summarize_trace(trace_dir, workload, steps, warmup, command):
 
 # Steps per chunk of the event-timed pass (see the comment there).
 EVENT_CHUNK_STEPS = 10
+# Untimed steps of the same part that run between each chunk's pre-roll and
+# its timed steps: about this much GPU time (from three steps timed after the
+# warmup), at least 2 and at most 80 steps.
+# After the idle pre-roll the card's clock goes through a transient under a
+# sudden MFMA load (a prefix-hit prefill call goes ~540 -> ~720 -> ~505 us
+# over its first ~30 ms of back-to-back calls); the settle steps let it pass,
+# so the timed calls see the clock of continuous work.
+EVENT_SETTLE_S = 0.06
+EVENT_SETTLE_MAX = 80
 
 
 def preroll_cycles(seconds: float) -> int:
@@ -900,6 +922,9 @@ def main():
                     help="print the issue-rate probes (libpkv_probe) as markdown and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("PMC_DIR", "COMMAND"),
                     help="per-kernel means of a rocprofv3 --pmc run, then exit")
+    ap.add_argument("--trace-settle", default="",
+                    help="with --summarize-trace: the traced run's settle steps per chunk, by part "
+                         "(event_timing.settle_steps_per_chunk of its bench line), comma-separated")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
                     help="per-workload kernel durations of a rocprofv3 --kernel-trace run of "
                          "the bench with the same --workload/--steps/--warmup, then exit")
@@ -915,7 +940,8 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.workload, args.steps, args.warmup,
-                        args.summarize_trace[1])
+                        args.summarize_trace[1],
+                        [int(x) for x in args.trace_settle.split(",")] if args.trace_settle else None)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -942,7 +968,8 @@ def main():
     log(f"[bench] 1 GiB device copy: {copy_gbps:.0f} GB/s (read + write)")
     stream_read = stream_read_rates()
     log(f"[bench] 2 GiB read-only stream: plain {stream_read['plain']['GBps']:.0f} GB/s, "
-        f"decode-shaped {stream_read['decode_shaped']['GBps']:.0f} GB/s")
+        f"decode-shaped {stream_read['decode_shaped']['GBps']:.0f} GB/s, "
+        f"span {stream_read['span']['GBps']:.0f} GB/s")
     if args.copy_calibration:
         src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -959,9 +986,16 @@ def main():
     # which would hide its own speed). A step is one step of each workload.
     order = lambda base: [(base + i, p) for p in parts for i in range(args.steps)]
     log("[bench] warmup")
-    metas = [p.run(i, None) for p in parts for i in range(args.warmup)]
-    torch.cuda.synchronize()
-    del metas
+    step_s = []   # a part's step on the GPU after its warmup (sets its settle count)
+    for p in parts:
+        metas = [p.run(i, None) for i in range(args.warmup)]
+        torch.cuda.synchronize()
+        t_w = time.perf_counter()
+        n_cal = min(3, args.warmup + args.steps)   # metadata buffers the warmup has finished with
+        metas += [p.run(i, None) for i in range(n_cal)]
+        torch.cuda.synchronize()
+        step_s.append((time.perf_counter() - t_w) / n_cal)
+        del metas
 
     # Whole steps, wall clock: host packing, uploads and every kernel, with a
     # synchronize on both sides. The objects made during set-up (torch's own
@@ -985,9 +1019,14 @@ def main():
     # The pass goes in chunks of a few steps, each behind its own spin and
     # followed by a synchronize: with hundreds of commands outstanding the
     # runtime makes the host wait for queue space, and the GPU would then
-    # idle inside the timed intervals.
-    for p in parts:
-        p.prepare(args.steps)
+    # idle inside the timed intervals. Between the spin and the timed steps
+    # of a chunk, untimed steps of the same part (EVENT_SETTLE_S of GPU time)
+    # take the card from the idle spin to the clock it holds under
+    # continuous work.
+    chunk = EVENT_CHUNK_STEPS
+    settle = [int(min(EVENT_SETTLE_MAX, max(2, math.ceil(EVENT_SETTLE_S / max(t, 1e-6))))) for t in step_s]
+    for p, n_settle in zip(parts, settle):
+        p.prepare(args.steps + n_settle)   # the settle steps use their own metadata buffers
     events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in parts]
               for _ in range(args.steps)]
     # torch creates the HIP event on its first record: do that outside the
@@ -997,15 +1036,15 @@ def main():
             for e in evs:
                 e.record()
     torch.cuda.synchronize()
-    chunk = EVENT_CHUNK_STEPS
-    preroll_s = 4 * t_host * chunk / args.steps + 5e-3
-    cycles = preroll_cycles(preroll_s)
     t_enq_max, late = 0.0, 0
-    for p in parts:
+    for p, n_settle in zip(parts, settle):
+        preroll_s = 4 * t_host * (chunk + n_settle) / args.steps + 5e-3
+        cycles = preroll_cycles(preroll_s)
         for c0 in range(0, args.steps, chunk):
             torch.cuda._sleep(cycles)
             t_enq = time.perf_counter()
-            keep = [p.run(i, events[i][parts.index(p)]) for i in range(c0, min(c0 + chunk, args.steps))]
+            keep = [p.run(args.steps + j, None) for j in range(n_settle)]
+            keep += [p.run(i, events[i][parts.index(p)]) for i in range(c0, min(c0 + chunk, args.steps))]
             t_enq = time.perf_counter() - t_enq
             torch.cuda.synchronize()
             del keep
@@ -1016,7 +1055,7 @@ def main():
             "those intervals may hold host gaps")
     log(f"[bench] wall {wall * 1e3:.2f} ms for {args.steps} steps (host {t_host * 1e3:.1f} ms); "
         f"event pass in chunks of {chunk} steps: longest host enqueue {t_enq_max * 1e3:.2f} ms "
-        f"behind a {preroll_s * 1e3:.1f} ms pre-roll")
+        f"behind a {preroll_s * 1e3:.1f} ms pre-roll; settle steps per chunk {settle}")
     for j, p in enumerate(parts):
         p.collect([events[i][j] for i in range(args.steps)])
     summaries = [p.summary() for p in parts]
@@ -1075,7 +1114,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": config, "roofline": roof, "cpu_baseline": cpu_main,
         "secondary": {}, "parts": summaries, "cpu_baselines": cpu,
-        "event_timing": {"chunk_steps": EVENT_CHUNK_STEPS, "chunks_with_host_gaps": late},
+        "event_timing": {"chunk_steps": EVENT_CHUNK_STEPS, "chunks_with_host_gaps": late,
+                         "settle_steps_per_chunk": settle, "settle_target_s": EVENT_SETTLE_S},
     }
     if any(p.preset == 4 for p in parts):
         line["block_manager_host"] = block_manager_host()
@@ -1097,6 +1137,8 @@ def main():
                 "avg_launch_us": pre["attention_us"]}
     if dec is not None:
         sec["decode_frac_of_hbm_peak"] = dec["attention_frac_hbm"]
+        # the same call against the best read-only stream this GPU reached in this run
+        sec["decode_over_best_stream_read"] = dec["attention_GBps"] / stream_read["best"]["GBps"]
     # every part's attention figure, by workload
     for sm in summaries:
         k = names[sm["preset"]] + ("+fused-store" if sm["workload"].endswith("+fused") else "")

@@ -15,6 +15,8 @@
  *           head's 256-byte slices of 64 consecutive rows at a time (16 lanes
  *           per slice, 16 loads in flight per lane), as the decode kernel
  *           reads one kv head's K or V.
+ *   mode 2  span: the buffer is cut into one contiguous span per wave, which
+ *           the wave reads 1 KiB per load instruction with 16 loads in flight.
  *   blocks  workgroups of 256 threads to launch (> 0).
  * Returns 0, or 1 for bad arguments, 3 when the launch fails. Asynchronous on
  * `stream` (a hipStream_t as void*).

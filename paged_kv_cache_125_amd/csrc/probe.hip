@@ -65,6 +65,27 @@ __global__ __launch_bounds__(256) void stream_read_rows(const uint8_t *buf, int6
 }
 
 
+// Each wave reads one contiguous span of the buffer (spans in wave order),
+// 1 KiB per load instruction (64 lanes x 16 bytes), sixteen loads in flight.
+__global__ __launch_bounds__(256) void stream_read_span(const uint8_t *buf, int64_t n16, int32_t *sink) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t W = (int64_t)gridDim.x * 4;
+    const int64_t per = (n16 + W - 1) / W;               // 16-byte chunks per wave
+    const int64_t c0 = w * per, c1 = c0 + per < n16 ? c0 + per : n16;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    int64_t c = c0 + lane;
+    for (; c + 15 * 64 < c1; c += 16 * 64) {
+        u32x4 x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x[u] = ld16(buf + 16 * (c + 64 * u));
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc ^= x[u];
+    }
+    for (; c < c1; c += 64) acc ^= ld16(buf + 16 * c);
+    keep(acc, sink);
+}
+
 // ---------------------------------------------------------------------------
 // Issue-rate probes. One workgroup per CU (96 KiB of LDS keeps a second one
 // off), 4 * waves_per_simd waves, so wave w runs on SIMD w % 4 beside
@@ -284,6 +305,9 @@ extern "C" int pkv_probe_stream_read(const void *buf, size_t bytes, int32_t mode
         if (rows == 0) return 1;
         hipLaunchKernelGGL(stream_read_rows, dim3(blocks), dim3(256), 0, s, (const uint8_t *)buf,
                            rows, row_bytes / 256, row_bytes, sink);
+    } else if (mode == 2) {
+        hipLaunchKernelGGL(stream_read_span, dim3(blocks), dim3(256), 0, s, (const uint8_t *)buf,
+                           (int64_t)(bytes / 16), sink);
     } else {
         return 1;
     }

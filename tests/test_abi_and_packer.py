@@ -59,7 +59,7 @@ def test_probe_library_rejects_bad_arguments_before_any_launch():
     assert lib.pkv_probe_stream_read(buf, 4096, 0, 0, 0, sink, None) == 1      # no blocks
     assert lib.pkv_probe_stream_read(buf, 4096, 1, 300, 1, sink, None) == 1    # rows not 256-byte multiples
     assert lib.pkv_probe_stream_read(buf, 4096, 1, 8192, 1, sink, None) == 1   # fewer bytes than one row
-    assert lib.pkv_probe_stream_read(buf, 4096, 2, 0, 1, sink, None) == 1      # unknown mode
+    assert lib.pkv_probe_stream_read(buf, 4096, 3, 0, 1, sink, None) == 1      # unknown mode
 
 
 def test_library_exports_every_declared_symbol():
