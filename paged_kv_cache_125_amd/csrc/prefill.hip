@@ -12,7 +12,9 @@
 //
 // prefill_mfma_kernel (bf16, head_dim 128) is a FlashAttention-2 style forward
 // (Dao, 2023) laid out for CDNA4: a workgroup of 4 waves owns 128 query rows of
-// one head (32 per wave) and streams 64-key tiles of K and V through two LDS
+// one head (32 per wave) -- or, when every sequence is short, 64 or 32 rows of
+// each of 2 or 4 query heads of a GQA group, which then share every staged
+// K/V tile -- and streams 64-key tiles of K and V through two LDS
 // buffers (the next tile's global loads are in flight while the current one
 // is computed; one barrier per tile). Two workgroups per CU, so two waves
 // share each SIMD: while one waits on LDS or runs its softmax on the VALU,
@@ -86,17 +88,22 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, __attribute__
     (__builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, voff[I], 0, 1024 * I, 0), ...);
 }
 
-// NW waves per workgroup, RB blocks of 32 query rows per wave: the workgroup
-// owns BM = 32 * RB * NW rows of one query head. WPE waves share one SIMD.
+// NW waves per workgroup, RB blocks of 32 query rows per wave. HPW query
+// heads of one GQA group share the workgroup and every K/V tile it stages,
+// NW / HPW waves each: the workgroup owns BM = 32 * RB * NW / HPW rows of each
+// of its heads. WPE waves share one SIMD.
 // STORE: store_kvcache fused into the attention launch. Each query block
 // also copies its own rows of the call's k/v into the cache (shared out over
 // the group's query heads), and keys at positions Lk - Lq and beyond -- the
 // ones this call stores -- are read from those rows rather than the pool.
-template <int SRC, int NW, int RB, int WPE, bool PERSIST, bool STORE>
+template <int SRC, int NW, int RB, int WPE, bool PERSIST, bool STORE, int HPW>
 __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
     static_assert(!STORE || (RB == 1 && !PERSIST && SRC != kPoolSmall),
                   "the fused store is built for the fixed grid and tiles of whole 16-key slices");
-    constexpr int BM = 32 * RB * NW;         // query rows per workgroup (one query head)
+    static_assert(HPW == 1 || (!STORE && !PERSIST && NW % HPW == 0),
+                  "heads share a workgroup on the fixed grid of the attention-only kernel");
+    constexpr int WPH = NW / HPW;            // waves per query head
+    constexpr int BM = 32 * RB * WPH;        // query rows per workgroup and head
     constexpr int LPW = 16 / NW;   // 1 KiB direct-load instructions per wave per K (or V) tile
     static_assert(NW * LPW == 16 && NW >= 2, "waves must split a tile evenly");
     static_assert(RB == 1 || RB == 2, "row blocks per wave");
@@ -128,11 +135,11 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
     //    pairs' K/V are live at a time.
     // Either way the group's heads sit side by side and every (pair, query
     // block, head) is visited once.
-    const int HG = a.group;                  // query heads per kv head
+    const int HG = a.group / HPW;            // head groups per kv head
     const int qblocks = (a.max_seqlen_q + BM - 1) / BM;
     const int npairs = a.num_seqs * a.Hkv;
     const int xcd = blockIdx.x & 7;
-    const int wh = wave;                     // the wave's place in the workgroup's rows
+    const int hh = wave / WPH, wh = wave - hh * WPH;   // the wave's head in the group, its place in the head's rows
 
     // Persistent grid: the claim of the next item, issued by thread 0 once an
     // item's tile loop is done (so that the per-tile waits for vector memory
@@ -144,7 +151,7 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
     auto run_item = [&](const int pair, const int qt, const int hg) {
     const int s = pair / a.Hkv;
     const int kvh = pair - s * a.Hkv;
-    const int h = kvh * a.group + hg;
+    const int h = kvh * a.group + hg * HPW + hh;
     // Block-table entries are read through the scalar cache (a wave-uniform
     // index) one tile ahead of the loads that use them: a vector load here
     // would make every tile step wait for it (vmcnt counts in order) before
@@ -821,17 +828,17 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
     }
 }
 
-template <int SRC, int NW, int RB, int WPE, bool PERSIST>
+template <int SRC, int NW, int RB, int WPE, bool PERSIST, int HPW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_mfma_kernel(PrefillArgs a) {
-    prefill_mfma_body<SRC, NW, RB, WPE, PERSIST, false>(a);
+    prefill_mfma_body<SRC, NW, RB, WPE, PERSIST, false, HPW>(a);
 }
 
 // The call's K/V rows also stored into the cache.
 template <int SRC, int NW, int WPE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_store_mfma_kernel(PrefillArgs a) {
-    prefill_mfma_body<SRC, NW, 1, WPE, false, true>(a);
+    prefill_mfma_body<SRC, NW, 1, WPE, false, true, 1>(a);
 }
 
 template <typename T>
@@ -947,32 +954,42 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
         // waves per SIMD: while one wave waits on LDS or runs its softmax the
         // other keeps the matrix core busy.
         constexpr int NW = 4, RB = 1;
-        // One query head per workgroup, 128 rows. (Two heads of a GQA group
-        // sharing a workgroup's K/V tiles, 64 rows each, measured equal on
-        // prefix hits and 9% slower on a mixed step once the block-table
-        // reads were taken off the tile loop's critical path.)
+        // One query head per workgroup, 128 rows, when any sequence has more
+        // query rows than a shared workgroup would give each head: there two
+        // heads of a GQA group sharing a workgroup's K/V tiles (64 rows each)
+        // measured equal on prefix hits and 9% slower on a mixed step. When
+        // every sequence fits (decode rows, short chunks: at most 64 rows,
+        // or 32 with a group of 4), HPW heads share it and each K/V tile is
+        // staged once for all of them: 64 decode rows took 122 us this way
+        // against 168 us with one head per workgroup.
+        const bool store = a.slots && (!a.paged || a.bs >= 4 * (16 / NW));
+        const int hpw = store ? 1
+                        : (a.group % 4 == 0 && a.max_seqlen_q <= 32 * RB * (NW / 4)) ? 4
+                        : (a.group % 2 == 0 && a.max_seqlen_q <= 32 * RB * (NW / 2)) ? 2 : 1;
+        const int bm = 32 * RB * (NW / hpw);
         const int64_t pairs = (int64_t)a.num_seqs * a.Hkv;
-        const int64_t qblocks = (a.max_seqlen_q + 32 * RB * NW - 1) / (32 * RB * NW);
+        const int64_t qblocks = (a.max_seqlen_q + bm - 1) / bm;
         // The persistent grid (two workgroups per CU claiming items) only when
-        // the caller gave a workspace and the item tables fit in LDS.
-        const bool persist = a.work_ctr != nullptr && (pairs + 7) / 8 <= kPfMaxXcdPairs &&
+        // the caller gave a workspace, the item tables fit in LDS and every
+        // workgroup takes one head.
+        const bool persist = a.work_ctr != nullptr && hpw == 1 && (pairs + 7) / 8 <= kPfMaxXcdPairs &&
                              qblocks <= kPfMaxQblocks;
-        const int64_t nwg_fixed = 8 * ((pairs + 7) / 8) * qblocks * a.group;
+        const int64_t nwg_fixed = 8 * ((pairs + 7) / 8) * qblocks * (a.group / hpw);
         if (nwg_fixed > 0x7fffffff) return hipErrorInvalidValue;
         const int64_t nwg = persist ? 8 * ((2 * prefill_cus() + 7) / 8) : nwg_fixed;
         const dim3 grid((unsigned)nwg), block(64 * NW);
-#define PKV_MFMA_LAUNCH(P)                                                                                \
-    do {                                                                                                  \
-        if (!a.paged)                                                                                     \
-            hipLaunchKernelGGL((prefill_mfma_kernel<kContiguous, NW, RB, 2, P>), grid, block, 0, stream, a); \
-        else if (a.bs % kPfBN == 0)                                                                       \
-            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolBlocks, NW, RB, 2, P>), grid, block, 0, stream, a); \
-        else if (a.bs >= 4 * (16 / NW))                                                                   \
-            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolWave, NW, RB, 2, P>), grid, block, 0, stream, a);   \
-        else                                                                                              \
-            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2, P>), grid, block, 0, stream, a);  \
+#define PKV_MFMA_LAUNCH(P, H)                                                                                \
+    do {                                                                                                     \
+        if (!a.paged)                                                                                        \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kContiguous, NW, RB, 2, P, H>), grid, block, 0, stream, a); \
+        else if (a.bs % kPfBN == 0)                                                                          \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolBlocks, NW, RB, 2, P, H>), grid, block, 0, stream, a); \
+        else if (a.bs >= 4 * (16 / NW))                                                                      \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolWave, NW, RB, 2, P, H>), grid, block, 0, stream, a);   \
+        else                                                                                                 \
+            hipLaunchKernelGGL((prefill_mfma_kernel<kPoolSmall, NW, RB, 2, P, H>), grid, block, 0, stream, a);  \
     } while (0)
-        if (a.slots && (!a.paged || a.bs >= 4 * (16 / NW))) {
+        if (store) {
             const dim3 g((unsigned)nwg_fixed);
             if (!a.paged)
                 hipLaunchKernelGGL((prefill_store_mfma_kernel<kContiguous, NW, 2>), g, block, 0, stream, a);
@@ -986,11 +1003,17 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, hipStream_t stream) {
             // and was slower than the two launches.)
             const hipError_t e = launch_store_of(a, dtype, stream);
             if (e != hipSuccess) return e;
-            PKV_MFMA_LAUNCH(false);
+            if (hpw == 4) PKV_MFMA_LAUNCH(false, 4);
+            else if (hpw == 2) PKV_MFMA_LAUNCH(false, 2);
+            else PKV_MFMA_LAUNCH(false, 1);
         } else if (persist) {
-            PKV_MFMA_LAUNCH(true);
+            PKV_MFMA_LAUNCH(true, 1);
+        } else if (hpw == 4) {
+            PKV_MFMA_LAUNCH(false, 4);
+        } else if (hpw == 2) {
+            PKV_MFMA_LAUNCH(false, 2);
         } else {
-            PKV_MFMA_LAUNCH(false);
+            PKV_MFMA_LAUNCH(false, 1);
         }
 #undef PKV_MFMA_LAUNCH
     } else {

@@ -357,23 +357,27 @@ def test_mixed_batch(cuda, case):
 
 
 SHORT = [
-    # (num_q_heads, num_kv_heads, block_size): sequences of 1 to 33 query rows
-    # (all of a query block's live rows in its first wave, or one past it)
-    # across group sizes 1, 2, 3, 4 and 8; 0 = contiguous keys
-    (8, 8, 16), (16, 8, 256), (24, 8, 64), (32, 8, 16), (64, 8, 256), (16, 8, 0), (24, 8, 0),
+    # (num_q_heads, num_kv_heads, block_size, longest query): sequences of 1
+    # to 33 (or 32) query rows (all of a query block's live rows in its first
+    # wave, or one past it) across group sizes 1, 2, 3, 4 and 8; 0 = contiguous
+    # keys. Batches whose sequences all fit one shared query block put 2 (at
+    # most 64 rows) or 4 (at most 32 rows, groups of 4 and 8) query heads of a
+    # group in one workgroup; the 32-row cases reach the 4-head form.
+    (8, 8, 16, 33), (16, 8, 256, 33), (24, 8, 64, 33), (32, 8, 16, 33), (64, 8, 256, 33), (16, 8, 0, 33),
+    (24, 8, 0, 33), (32, 8, 16, 32), (64, 8, 256, 32), (32, 8, 0, 32), (16, 8, 64, 32),
 ]
 
 
-@pytest.mark.parametrize("case", SHORT, ids=lambda c: f"g{c[0] // c[1]}-bs{c[2]}")
+@pytest.mark.parametrize("case", SHORT, ids=lambda c: f"g{c[0] // c[1]}-bs{c[2]}-q{c[3]}")
 def test_short_sequences(cuda, case):
-    hq, hkv, bs = case
+    hq, hkv, bs, longest = case
     if bs:
-        # query rows 1, 5, 31, 32, 33 and 1 against contexts of 1 to ~2.2k keys
+        # query rows 1, 5, 31, 32, 33 (or 1) and 1 against contexts of 1 to ~2.2k keys
         lens = [1, 700, 2100, 64, 97, 2200]
-        lq = [1, 5, 31, 32, 33, 1]
+        lq = [1, 5, 31, 32, 33 if longest == 33 else 1, 1]
     else:
         # fresh prompts (contiguous keys): Lk = Lq
-        lens = [1, 5, 31, 32, 33, 17]
+        lens = [1, 5, 31, 32, 33 if longest == 33 else 1, 17]
         lq = lens
     cached = [n - q for n, q in zip(lens, lq)]
     say(f"[gpu] short sequences Hq {hq} Hkv {hkv} bs {bs}: lens {lens} cached {cached}")
