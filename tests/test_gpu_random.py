@@ -7,7 +7,9 @@ enough for the oracle; the tolerance is the attention bar (2e-2 bf16, 1e-4
 fp32) and the pools are compared bit for bit. The prefill shapes (with their
 cached prefixes) also go through prefill_store_attention_varlen, which must
 match the oracle and equal the separate store and attention calls bit for
-bit."""
+bit. A further set draws short batches (every sequence's query rows capped at
+1, 8, 32 or 64, even groups), the batches whose query heads share a workgroup
+two or four at a time, over every key source."""
 import numpy as np
 import pytest
 import torch
@@ -116,3 +118,37 @@ def test_random_fused_store_prefill(cuda, i):
     err = max_abs_err(of, want)
     say(f"  max |err| = {err:.3e}")
     assert err <= TOL[dt]
+
+
+def short_prefill_case(i):
+    """bf16, head_dim 128 (the MFMA kernel), even GQA groups, and query rows
+    capped at 1, 8, 32 or 64 for every sequence: the batches that put 2 or 4
+    query heads of a group in one workgroup, over every key source."""
+    rng = np.random.default_rng(6000 + i)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([2, 4, 6, 8]))
+    bs = int(rng.choice([0, 4, 8, 16, 32, 64, 256]))   # 0: contiguous keys (no cached prefix)
+    cap = int(rng.choice([1, 8, 32, 64]))
+    s = int(rng.integers(1, 9))
+    if bs == 0:
+        lens = [int(x) for x in rng.integers(1, cap + 1, s)]
+        cached = [0] * s
+    else:
+        lens = [int(x) for x in rng.integers(1, 2001, s)]
+        cached = [max(0, n - int(rng.integers(1, cap + 1))) for n in lens]
+    return lens, cached, hkv * group, hkv, bs
+
+
+@pytest.mark.parametrize("i", range(24), ids=lambda i: f"pf-short-r{i}")
+def test_random_short_prefill(cuda, i):
+    lens, cached, hq, hkv, bs = short_prefill_case(i)
+    say(f"[gpu] random short prefill {i}: lens {lens} cached {cached} Hq {hq} Hkv {hkv} bs {bs}")
+    w = custom_workload(phase="prefill", seq_lens=lens, num_cached=cached, num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=128, block_size=bs or 16, dtype=torch.bfloat16,
+                        seed=290 + i)
+    out, kc, vc = gpu_run(to_device(w, "cuda"))
+    want, kp, vp, _ = oracle.run_workload(w)
+    assert np.array_equal(raw(kc), raw(kp)) and np.array_equal(raw(vc), raw(vp))
+    err = max_abs_err(out, want)
+    say(f"  max |err| = {err:.3e}")
+    assert err <= TOL[torch.bfloat16]
