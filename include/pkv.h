@@ -130,9 +130,12 @@ int pkv_store_kvcache(const void *k, const void *v, int64_t k_token_stride,
  *  max_seqlen_q/_k host upper bounds of Lq_s / Lk_s (size the launch grid).
  *  dtype           PKV_BF16 (MFMA path for head_dim 128) or PKV_F32.
  *  workspace       NULL (with workspace_bytes 0): one workgroup per
- *                  (sequence, kv head, query block) item, laid out longest
- *                  first so that the hardware's own dispatch balances the
- *                  batch. Non-NULL: device memory of
+ *                  (sequence, kv head, query block, query head) item, laid
+ *                  out longest first so that the hardware's own dispatch
+ *                  balances the batch; when no sequence has more than 64
+ *                  query rows (32 with a group of 4 or more), 2 (or 4)
+ *                  query heads of a GQA group share an item and every K/V
+ *                  tile it stages. Non-NULL: device memory of
  *                  pkv_prefill_workspace_bytes() bytes, 256-byte aligned,
  *                  ZEROED ONCE when it is allocated, holding the counters of
  *                  the persistent grid: two workgroups per CU whatever the
@@ -141,8 +144,9 @@ int pkv_store_kvcache(const void *k, const void *v, int64_t k_token_stride,
  *                  call without clearing; calls that may run at the same time
  *                  (on different streams) need workspaces of their own.
  *                  Batches beyond the persistent grid's tables (more than
- *                  2048 (sequence, kv head) pairs or 512 query blocks) take
- *                  one workgroup per item and leave the workspace untouched.
+ *                  2048 (sequence, kv head) pairs or 512 query blocks), and
+ *                  batches whose query heads share items, take one
+ *                  workgroup per item and leave the workspace untouched.
  *                  Both grids give bit-identical results; on the batches
  *                  measured so far the one-workgroup-per-item grid is the
  *                  faster one. Only the bf16 head_dim-128 kernel has the
