@@ -86,6 +86,13 @@ __global__ __launch_bounds__(256) void stream_read_span(const uint8_t *buf, int6
     keep(acc, sink);
 }
 
+// Workgroup b writes the id of the XCD (XCC) it runs on: hardware register
+// XCC_ID (hwreg 20), bits [3:0]. One store per workgroup, b < n only.
+__global__ __launch_bounds__(64) void xcc_of_workgroup(int32_t *out, int32_t n) {
+    if (threadIdx.x == 0 && (int32_t)blockIdx.x < n)
+        out[blockIdx.x] = (int32_t)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u);
+}
+
 // ---------------------------------------------------------------------------
 // Issue-rate probes. One workgroup per CU (96 KiB of LDS keeps a second one
 // off), 4 * waves_per_simd waves, so wave w runs on SIMD w % 4 beside
@@ -343,4 +350,10 @@ extern "C" int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blo
         case 17: e = launch_issue<17>(blocks, waves, cycles, sink, s); break;
     }
     return e == hipSuccess ? 0 : 3;
+}
+
+extern "C" int pkv_probe_xcc(int32_t *out, int32_t n, void *stream) {
+    if (!out || n <= 0) return 1;
+    hipLaunchKernelGGL(xcc_of_workgroup, dim3((unsigned)n), dim3(64), 0, (hipStream_t)stream, out, n);
+    return hipGetLastError() == hipSuccess ? 0 : 3;
 }

@@ -28,7 +28,7 @@ def test_probe_library_exports_every_declared_symbol():
     from paged_kv_cache_125_amd.build import PROBE_LIB
     src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pkv_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", src)))
-    assert names == ["pkv_probe_issue", "pkv_probe_stream_read"]
+    assert names == ["pkv_probe_issue", "pkv_probe_stream_read", "pkv_probe_xcc"]
     lib = ctypes.CDLL(PROBE_LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -60,6 +60,10 @@ def test_probe_library_rejects_bad_arguments_before_any_launch():
     assert lib.pkv_probe_stream_read(buf, 4096, 1, 300, 1, sink, None) == 1    # rows not 256-byte multiples
     assert lib.pkv_probe_stream_read(buf, 4096, 1, 8192, 1, sink, None) == 1   # fewer bytes than one row
     assert lib.pkv_probe_stream_read(buf, 4096, 3, 0, 1, sink, None) == 1      # unknown mode
+    lib.pkv_probe_xcc.restype = ctypes.c_int
+    lib.pkv_probe_xcc.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert lib.pkv_probe_xcc(None, 8, None) == 1                               # no output
+    assert lib.pkv_probe_xcc(sink, 0, None) == 1                               # no workgroups
 
 
 def test_library_exports_every_declared_symbol():

@@ -1,8 +1,9 @@
 """GPU tests of the prefill grids. The persistent grid (a fixed set of
 workgroups claiming items from counters in the caller's workspace) against
 the oracle and against the one-workgroup-per-item grid; the workspace left
-zeroed after every call, so it is reused without clearing; and batches past
-the persistent grid's table limits, which take the fixed grid."""
+zeroed after every call, so it is reused without clearing; batches past
+the persistent grid's table limits, which take the fixed grid; and the
+hardware's workgroup-to-XCD placement both grids' orders assume."""
 import numpy as np
 import pytest
 import torch
@@ -98,3 +99,22 @@ def test_batch_past_the_table_limit_takes_the_fixed_grid(cuda):
     err = max_abs_err(got, want)
     say(f"  max |err| = {err:.3e}")
     assert err <= 2e-2 and bool((ws == 0).all())
+
+
+@pytest.mark.parametrize("n", [512, 1000, 4096])
+def test_workgroups_land_on_xcd_blockidx_mod_8(cuda, n):
+    # The grid order of both prefill grids puts a (sequence, kv head) pair's
+    # items on one XCD by assuming the hardware hands workgroup b to XCD
+    # b % 8 (so that they share that XCD's L2); libpkv_probe reads each
+    # workgroup's XCC_ID register to check it.
+    import ctypes
+    from paged_kv_cache_125_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pkv_probe_xcc.restype = ctypes.c_int
+    lib.pkv_probe_xcc.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    say(f"[gpu] XCD of each of {n} workgroups")
+    out = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.pkv_probe_xcc(ctypes.c_void_p(out.data_ptr()), n, stream) == 0
+    got = out.cpu().numpy()
+    assert np.array_equal(got, np.arange(n) % 8), got[:32]
