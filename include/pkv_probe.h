@@ -65,8 +65,10 @@ int pkv_probe_issue(int32_t mode, int32_t waves_per_simd, int32_t blocks, uint64
 
 /* pkv_probe_xcc launches n workgroups (n > 0) and has workgroup b write the
  * id of the XCD it runs on (the XCC_ID hardware register) to out[b] (device
- * memory, n int32). The prefill kernel's grid order assumes the hardware
- * hands workgroup b to XCD b % 8; this checks it. Returns 0, 1 for bad
+ * memory, n int32). The prefill kernel's grid order assumes that the
+ * hardware deals workgroups to the 8 XCDs round robin, so that workgroups
+ * with equal b % 8 share an XCD (the first one's XCD depends on earlier
+ * launches); this checks it. Returns 0, 1 for bad
  * arguments, 3 when the launch fails. Asynchronous on `stream`. */
 int pkv_probe_xcc(int32_t *out, int32_t n, void *stream);
 

@@ -123,11 +123,12 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Work order, XCD-aware. The hardware hands workgroup p to XCD p % 8, and
-    // each XCD has its own L2. Work is grouped by (sequence, kv head) pair,
-    // the unit that shares K and V; pair pi runs on XCD pi % 8, so all query
-    // blocks and all query heads of that kv head read their K/V tiles through
-    // one L2. Two orders within an XCD, chosen on the host from the batch's
+    // Work order, XCD-aware. The hardware deals a launch's workgroups to the 8
+    // XCDs round robin (starting wherever the previous launch left off), so
+    // workgroups with equal p % 8 run on one XCD, and each XCD has its own
+    // L2. Work is grouped by (sequence, kv head) pair, the unit that shares K
+    // and V; pair pi runs on the XCD of class pi % 8, so all query blocks and
+    // all query heads of that kv head read their K/V tiles through one L2. Two orders within an XCD, chosen on the host from the batch's
     // K/V bytes (a bound on them when the keys come through block tables):
     //  - K/V within half the 256 MB MALL: longest first across all the XCD's
     //    pairs (query-block rank major), so the tail holds only short blocks;
@@ -681,11 +682,12 @@ __device__ __forceinline__ void prefill_mfma_body(const PrefillArgs &a) {
     };
 
     if constexpr (!PERSIST) {
-        // One workgroup per item, in a fixed XCD-aware order. The hardware
-        // hands workgroup p to XCD p % 8, and each XCD has its own L2. Work is
-        // grouped by (sequence, kv head) pair, the unit that shares K and V;
-        // pair pi runs on XCD pi % 8, so all query blocks and heads of that kv
-        // head read their K/V tiles through one L2. Two orders within an XCD,
+        // One workgroup per item, in a fixed XCD-aware order. Workgroups with
+        // equal p % 8 run on one XCD (the hardware deals them round robin),
+        // and each XCD has its own L2. Work is grouped by (sequence, kv head)
+        // pair, the unit that shares K and V; pair pi runs in class pi % 8, so
+        // all query blocks and heads of that kv head read their K/V tiles
+        // through one L2. Two orders within an XCD,
         // chosen on the host from the batch's K/V bytes (a bound on them when
         // the keys come through block tables):
         //  - K/V within half the 256 MB MALL: longest first across all the

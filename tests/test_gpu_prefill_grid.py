@@ -104,9 +104,12 @@ def test_batch_past_the_table_limit_takes_the_fixed_grid(cuda):
 @pytest.mark.parametrize("n", [512, 1000, 4096])
 def test_workgroups_land_on_xcd_blockidx_mod_8(cuda, n):
     # The grid order of both prefill grids puts a (sequence, kv head) pair's
-    # items on one XCD by assuming the hardware hands workgroup b to XCD
-    # b % 8 (so that they share that XCD's L2); libpkv_probe reads each
-    # workgroup's XCC_ID register to check it.
+    # items on one XCD by assuming the hardware deals a launch's workgroups to
+    # the 8 XCDs round robin, so that workgroups with equal b % 8 share an XCD
+    # and its L2. The first workgroup's XCD carries over from earlier launches
+    # (the rotation does not restart at 0), so the check is that the XCD of
+    # workgroup b is (b + s) % 8 for one s. libpkv_probe reads each
+    # workgroup's XCC_ID register.
     import ctypes
     from paged_kv_cache_125_amd.build import PROBE_LIB
     lib = ctypes.CDLL(PROBE_LIB)
@@ -117,4 +120,7 @@ def test_workgroups_land_on_xcd_blockidx_mod_8(cuda, n):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     assert lib.pkv_probe_xcc(ctypes.c_void_p(out.data_ptr()), n, stream) == 0
     got = out.cpu().numpy()
-    assert np.array_equal(got, np.arange(n) % 8), got[:32]
+    assert ((got >= 0) & (got < 8)).all(), got[:32]
+    shift = (got - np.arange(n)) % 8
+    assert (shift == shift[0]).all(), got[:32]
+    say(f"  workgroup b on XCD (b + {int(shift[0])}) % 8")
