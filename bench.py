@@ -22,7 +22,9 @@ attention. The default step holds, in this order:
 `value` is the long-context decode attention's algorithmic HBM throughput
 (GB/s); the prefix-hit prefill attention's TFLOP/s and fraction of the bf16
 MFMA peak sit beside it. Each call is timed with HIP events on the stream it
-runs on. Several copies of the inputs are used in rotation so that no step
+runs on, after untimed calls of the same kind have taken the card's clock to
+the state it holds under continuous work (EVENT_SETTLE_S). Several copies of
+the inputs are used in rotation so that no step
 finds its data in the 256 MB last-level cache. A read-only streaming kernel
 (libpkv_probe) is timed on a 2 GiB buffer in the same run, as an achievable
 reference beside the published HBM peak, and at each part's own byte counts
