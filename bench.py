@@ -395,9 +395,13 @@ def decode_graph_compare(num_layers: int = 28, batches=(1, 8, 64), steps: int = 
         maxb = max(len(t) for t in w.block_tables)
         g = DecodeGraphs(layers, w.num_q_heads, max_context_len=4096, max_blocks_per_seq=maxb,
                          scale=w.scale, buckets=[bucket_for(B)])
+        # the same graphs with the store as a call of its own in every layer
+        g2 = DecodeGraphs(layers, w.num_q_heads, max_context_len=4096, max_blocks_per_seq=maxb,
+                          scale=w.scale, buckets=[bucket_for(B)], fuse_store=False)
         qs, ks, vs = [w.q] * num_layers, [w.k_new] * num_layers, [w.v_new] * num_layers
         meta = pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cuda")
         g.prepare(qs, ks, vs, meta["slot_mapping"], meta["context_lens"], meta["block_tables"])
+        g2.prepare(qs, ks, vs, meta["slot_mapping"], meta["context_lens"], meta["block_tables"])
 
         def eager():
             m = pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cuda")
@@ -408,8 +412,13 @@ def decode_graph_compare(num_layers: int = 28, batches=(1, 8, 64), steps: int = 
             m = pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cuda")
             g.replay(g.prepare_meta(m["slot_mapping"], m["context_lens"], m["block_tables"]))
 
+        def graph_two_calls():
+            m = pkv.pack_decode(w.seq_lens, w.block_tables, w.block_size, device="cuda")
+            g2.replay(g2.prepare_meta(m["slot_mapping"], m["context_lens"], m["block_tables"]))
+
         times = {}
-        for name, fn in (("eager", eager), ("graph", graph), ("eager", eager), ("graph", graph)):
+        for name, fn in (("eager", eager), ("graph", graph), ("graph_two_calls", graph_two_calls),
+                         ("eager", eager), ("graph", graph), ("graph_two_calls", graph_two_calls)):
             for _ in range(3):
                 fn()
             torch.cuda.synchronize()
@@ -419,13 +428,16 @@ def decode_graph_compare(num_layers: int = 28, batches=(1, 8, 64), steps: int = 
             torch.cuda.synchronize()
             times[name] = (time.perf_counter() - t0) / steps * 1e3   # the second round counts
         res[f"B{B}"] = {"eager_ms_per_step": times["eager"], "graph_ms_per_step": times["graph"],
+                        "graph_two_calls_ms_per_step": times["graph_two_calls"],
                         "speedup": times["eager"] / times["graph"], "bucket": bucket_for(B),
                         "context_tokens": int(sum(w.seq_lens))}
-        del layers, g
+        del layers, g, g2
         torch.cuda.empty_cache()
     return {"layers": num_layers, "per_batch": res,
             "note": "decode attention side of one step (store + attention per layer) for the first B "
-                    "sequences of preset 2; wall clock per step incl. metadata pack+upload"}
+                    "sequences of preset 2; wall clock per step incl. metadata pack+upload; eager and "
+                    "graph use the fused store + decode call per layer, graph_two_calls a store call "
+                    "and a decode call"}
 
 
 # ----------------------------------------------------------------- oracle side

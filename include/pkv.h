@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 
 typedef enum {
     PKV_OK = 0,
@@ -313,6 +313,41 @@ int pkv_decode_attention_paged_noalloc(const void *q, int64_t q_token_stride, co
                                        int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, float scale, int32_t dtype, void *out,
                                        int32_t partition_size, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * store_kvcache and decode_attention_paged in one call: the decode step of a
+ * layer writes each sequence's new K/V row through slot_mapping and then
+ * attends over the context including it ([MR] ModelRunner init: attention
+ * writes new K/V through slot_mapping and reads history through
+ * block_tables; "prepare_decode": slot_mapping holds the slot of each
+ * sequence's last position and context_lens counts it).
+ *  k, v            the new tokens' rows [num_seqs, num_kv_heads, head_dim],
+ *                  kv_token_stride elements between sequences (16-byte
+ *                  aligned); row b is sequence b's token.
+ *  slot_mapping    int32 [num_seqs]: the slot of row b, negative to skip it.
+ *  The other arguments, the workspace and the errors are those of
+ *  pkv_decode_attention_paged (the caches are written).
+ * The result -- out and both caches -- equals pkv_store_kvcache(k, v,
+ * kv_token_stride, kv_token_stride, k_cache, v_cache, slot_mapping, num_seqs,
+ * ...) followed by pkv_decode_attention_paged(...) on the same stream,
+ * provided slot_mapping[b] is the slot of position context_lens[b] - 1 of
+ * sequence b through its block table (as pkv_pack_decode lays them out) or
+ * negative. On the fixed-partition bf16 path (head_dim 128, block_size a
+ * multiple of 64, the partition sizes small batches take) the store runs
+ * inside the attention launch: the wave holding a sequence's last position
+ * writes that token's row of its kv head before it reads the slot. Other
+ * shapes and the balanced split run the store kernel, then the attention.
+ * -------------------------------------------------------------------------*/
+int pkv_decode_store_attention_paged(const void *q, int64_t q_token_stride, const void *k,
+                                     const void *v, int64_t kv_token_stride, void *k_cache,
+                                     void *v_cache, const int32_t *slot_mapping,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *context_lens, int32_t num_seqs,
+                                     int32_t max_context_len, int32_t num_blocks,
+                                     int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, float scale, int32_t dtype, void *out,
+                                     int32_t partition_size, void *workspace,
+                                     size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Rotary embedding fused with store_kvcache (the step just before the KV write

@@ -28,7 +28,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpkv.so")
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 PKV_F32, PKV_BF16 = 0, 1
 # partition_size for decode_attention_paged: force the balanced split where the shape allows it
@@ -38,7 +38,7 @@ _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_ELAUNCH"
 EXPORTED = [
     "pkv_abi_version", "pkv_last_error", "pkv_store_kvcache", "pkv_prefill_attention_varlen",
     "pkv_decode_attention_paged", "pkv_decode_partition_size", "pkv_decode_workspace_bytes",
-    "pkv_decode_attention_paged_noalloc", "pkv_prefill_workspace_bytes",
+    "pkv_decode_attention_paged_noalloc", "pkv_decode_store_attention_paged", "pkv_prefill_workspace_bytes",
     "pkv_prefill_store_attention_varlen",
     "pkv_plan_prefill", "pkv_pack_prefill", "pkv_plan_decode", "pkv_pack_decode", "pkv_upload",
     "pkv_rope_cos_sin_table", "pkv_rope_store_kvcache",
@@ -95,6 +95,9 @@ def lib():
     L.pkv_decode_attention_paged.restype = ctypes.c_int
     L.pkv_decode_attention_paged.argtypes = [P, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32,
                                              i32, f32, i32, P, i32, P, sz, P]
+    L.pkv_decode_store_attention_paged.restype = ctypes.c_int
+    L.pkv_decode_store_attention_paged.argtypes = [P, i64, P, P, i64, P, P, P, P, i32, P, i32, i32, i32,
+                                                   i32, i32, i32, i32, f32, i32, P, i32, P, sz, P]
     L.pkv_decode_attention_paged_noalloc.restype = ctypes.c_int
     L.pkv_decode_attention_paged_noalloc.argtypes = [P, i64, P, P, P, i32, P, i32, i32, i32, i32, i32,
                                                      i32, i32, f32, i32, P, i32, P]
@@ -576,6 +579,49 @@ def decode_attention_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         int(block_tables.shape[1]), _ptr(context_lens), B, int(max_context_len), nb, bs, hq, hkv, d,
         float(scale), _dtype_code(q), _ptr(out), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    return out
+
+
+def decode_store_attention_paged(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                 k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                                 context_lens: torch.Tensor, max_context_len: int, scale: float, *,
+                                 out: Optional[torch.Tensor] = None, partition_size: int = 0,
+                                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pkv_decode_store_attention_paged: store_kvcache of k/v [B, Hkv, d] at
+    slot_mapping, then decode_attention_paged, in one call (one launch on the
+    fixed-partition path). k and v must share one token stride."""
+    _need(q.dim() == 3, "q must be [num_seqs, num_q_heads, head_dim]")
+    _need(q.dtype in _ATTN_DTYPES, lambda: f"unsupported dtype {q.dtype}")
+    B, hq, d = q.shape
+    _rows(q, "q", hq, d, q.dtype, 0)
+    _pool(k_cache, v_cache, q.dtype)
+    nb, bs, hkv, _ = k_cache.shape
+    _need(k_cache.shape[3] == d, "cache head_dim differs from q's")
+    _rows(k, "k", hkv, d, q.dtype, B)
+    _rows(v, "v", hkv, d, q.dtype, B)
+    _need(_token_stride(k) == _token_stride(v), "k and v must share one token stride")
+    _int32_vec(slot_mapping, "slot_mapping", B)
+    _int32_table(block_tables, "block_tables", B)
+    _int32_vec(context_lens, "context_lens", B)
+    if out is not None:
+        _out(out, q)
+    if workspace is not None:
+        _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(),
+              "workspace must be a contiguous uint8 tensor")
+    _one_gpu(q=q, k=k, v=v, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping,
+             block_tables=block_tables, context_lens=context_lens, out=out, workspace=workspace)
+    if out is None:
+        out = _alloc_on(stream, (B, hq, d), dtype=q.dtype, device=q.device)
+    need = decode_workspace_bytes(B, max_context_len, hq, hkv, d, bs, q.dtype, partition_size)
+    if workspace is None and need > 0:
+        workspace = _alloc_on(stream, need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_decode_store_attention_paged(
+        _ptr(q), _token_stride(q), _ptr(k), _ptr(v), _token_stride(k), _ptr(k_cache), _ptr(v_cache),
+        _ptr(slot_mapping), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
+        int(max_context_len), nb, bs, hq, hkv, d, float(scale), _dtype_code(q), _ptr(out),
+        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

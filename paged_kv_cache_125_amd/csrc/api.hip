@@ -396,7 +396,8 @@ int decode_call(const char *fn, const void *q, int64_t q_token_stride, const voi
                 const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
                 int32_t num_blocks, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
                 int32_t head_dim, float scale, int32_t dtype, void *out, int32_t partition_size,
-                void *workspace, size_t workspace_bytes, bool use_scratch, void *stream) {
+                void *workspace, size_t workspace_bytes, bool use_scratch, void *stream,
+                const pkv::StoreArgs *st = nullptr) {
     int rc = check_attention_shape(fn, dtype, num_q_heads, num_kv_heads, head_dim, num_seqs, scale);
     if (rc) return rc;
     if (max_context_len < 0) return fail(PKV_EINVAL, "%s: negative max_context_len", fn);
@@ -453,6 +454,22 @@ int decode_call(const char *fn, const void *q, int64_t q_token_stride, const voi
     a.ws_acc = ws.total ? (float *)workspace : nullptr;
     a.ws_ml = ws.total ? (float *)((char *)workspace + ws.acc_bytes) : nullptr;
     a.ws_cum = ws.cum_bytes ? (int32_t *)((char *)workspace + ws.acc_bytes + ws.ml_bytes) : nullptr;
+    if (st) {
+        // Fused where the fixed-partition kernel runs; otherwise the store
+        // kernel first, on the same stream, then the attention.
+        if (pkv::decode_store_fusable(a, ws, dtype)) {
+            a.st_k = st->k;
+            a.st_v = st->v;
+            a.st_stride_bytes = st->k_stride_bytes;
+            a.st_kc = st->kc;
+            a.st_vc = st->vc;
+            a.st_slots = st->slots;
+            a.st_num_slots = st->num_slots;
+        } else {
+            rc = launched(pkv::launch_store(*st, (hipStream_t)stream), fn);
+            if (rc) return rc;
+        }
+    }
     return launched(pkv::launch_decode(a, ws, dtype, (hipStream_t)stream), fn);
 }
 
@@ -480,6 +497,44 @@ extern "C" int pkv_decode_attention_paged_noalloc(
                        block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
                        num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, scale, dtype,
                        out, partition_size, nullptr, 0, true, stream);
+}
+
+extern "C" int pkv_decode_store_attention_paged(
+    const void *q, int64_t q_token_stride, const void *k, const void *v, int64_t kv_token_stride,
+    void *k_cache, void *v_cache, const int32_t *slot_mapping, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+    int32_t max_context_len, int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, float scale, int32_t dtype, void *out,
+    int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "pkv_decode_store_attention_paged";
+    if (!dtype_ok(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
+    if (num_seqs > 0) {
+        if (!k || !v || !slot_mapping) return fail(PKV_EINVAL, "%s: null k, v or slot_mapping", fn);
+        if (num_kv_heads <= 0 || head_dim <= 0) return fail(PKV_EINVAL, "%s: non-positive shape", fn);
+        const int es = elem_size(dtype);
+        const int64_t row = (int64_t)num_kv_heads * head_dim;
+        if ((row * es) % 16) return fail(PKV_EUNSUPPORTED, "%s: row bytes not a multiple of 16", fn);
+        if (kv_token_stride < row) return fail(PKV_EINVAL, "%s: k/v token stride smaller than a row", fn);
+        if ((kv_token_stride * es) % 16) return fail(PKV_EINVAL, "%s: k/v token stride not a multiple of 16 bytes", fn);
+        if (!aligned16(k) || !aligned16(v)) return fail(PKV_EINVAL, "%s: k/v must be 16-byte aligned", fn);
+        if (block_size <= 0 || num_blocks <= 0 || (int64_t)num_blocks * block_size > INT32_MAX)
+            return fail(PKV_EINVAL, "%s: pool shape", fn);
+    }
+    pkv::StoreArgs st;
+    const int es = elem_size(dtype);
+    st.k = (const uint8_t *)k;
+    st.v = (const uint8_t *)v;
+    st.k_stride_bytes = st.v_stride_bytes = kv_token_stride * es;
+    st.kc = (uint8_t *)k_cache;
+    st.vc = (uint8_t *)v_cache;
+    st.slots = slot_mapping;
+    st.num_tokens = num_seqs;
+    st.chunks_per_row = (int32_t)((int64_t)num_kv_heads * head_dim * es / 16);
+    st.num_slots = (int64_t)num_blocks * block_size;
+    return decode_call(fn, q, q_token_stride, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, max_context_len, num_blocks, block_size, num_q_heads,
+                       num_kv_heads, head_dim, scale, dtype, out, partition_size, workspace,
+                       workspace_bytes, false, stream, &st);
 }
 
 extern "C" int pkv_upload(const void *host_buf, void *dev_buf, size_t bytes, void *stream) {

@@ -279,7 +279,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_mfma_kernel(DecodeArgs 
 // Each lane owns one head column: the running max, its rescale factor and the
 // output accumulators are lane-local; only the max and the final sum cross
 // the 4 lane rows of a column.
-template <int G, int CH>
+//
+// STORE: store_kvcache fused into the launch. The wave that holds a
+// sequence's last position (its last partition; partition 0 for an empty
+// context) first writes that token's K and V rows of its kv head to the
+// token's slot, and waits for the writes before it issues any load, so its
+// own reads of that slot see them. Every kv head of every sequence is stored
+// once; padding slots (negative) and slots past the pool are skipped.
+template <int G, int CH, bool STORE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_blk_kernel(DecodeArgs a) {
     constexpr int D = 128;
@@ -297,6 +304,18 @@ void decode_blk_kernel(DecodeArgs a) {
     const int n = dec_ctx(a, b);
     const int t_begin = p * a.P;
     if (t_begin >= n && p > 0) return;
+    if constexpr (STORE) {
+        if (p == (n > 0 ? (n - 1) / a.P : 0)) {
+            const int slot = a.st_slots[b];
+            if ((uint32_t)slot < (uint64_t)a.st_num_slots && lane < D * 2 / 16) {
+                const int64_t src = (int64_t)b * a.st_stride_bytes + (int64_t)kvh * D * 2 + 16 * lane;
+                const int64_t dst = ((int64_t)slot * a.Hkv + kvh) * D * 2 + 16 * lane;
+                st16(a.st_kc + dst, ld16(a.st_k + src));
+                st16(a.st_vc + dst, ld16(a.st_v + src));
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // the row is written before this wave reads the slot
+        }
+    }
     const int nparts = (n + a.P - 1) / a.P;
     const int t_end = min(n, t_begin + a.P);
     const int lr = lane & 15, lg = lane >> 4;
@@ -1125,7 +1144,10 @@ static void launch_sk(const DecodeArgs &a, hipStream_t stream) {
 template <int G>
 static void launch_blk(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid((a.Hkv + 3) / 4, a.maxparts, a.num_seqs);
-    hipLaunchKernelGGL((decode_blk_kernel<G, kBlkChunk>), grid, dim3(256), 0, stream, a);
+    if (a.st_k)
+        hipLaunchKernelGGL((decode_blk_kernel<G, kBlkChunk, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_blk_kernel<G, kBlkChunk, false>), grid, dim3(256), 0, stream, a);
 }
 
 template <int G>
@@ -1135,8 +1157,14 @@ static void launch_mfma(const DecodeArgs &a, hipStream_t stream) {
                        stream, a);
 }
 
+bool decode_store_fusable(const DecodeArgs &a, const DecodePlan &plan, int dtype) {
+    return !plan.balanced && decode_has_blk_path(a, dtype) &&
+           (a.group == 1 || a.group == 2 || a.group == 4 || a.group == 8 || a.group == 16);
+}
+
 hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &plan, int dtype, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
+    if (a.st_k && !decode_store_fusable(a, plan, dtype)) return hipErrorInvalidValue;
     if (plan.balanced) {
         switch (a.group) {
             case 1: launch_sk<1>(a, stream); break;

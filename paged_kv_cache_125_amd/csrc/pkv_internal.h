@@ -56,6 +56,14 @@ struct DecodeArgs {
     float *ws_ml;              // the matching (max, sum) pairs
     int32_t *ws_cum;           // balanced split: chunk-count prefix sums [num_seqs + 1]
     int32_t waves;             // balanced split: waves in the grid
+    // Store fused into the fixed-partition kernel (null st_k otherwise): row b
+    // of st_k / st_v (st_stride_bytes apart) goes to slot st_slots[b] of
+    // st_kc / st_vc before the attention reads that slot.
+    const uint8_t *st_k = nullptr, *st_v = nullptr;
+    int64_t st_stride_bytes = 0;
+    uint8_t *st_kc = nullptr, *st_vc = nullptr;
+    const int32_t *st_slots = nullptr;
+    int64_t st_num_slots = 0;
 };
 // How a decode call is carried out, and the workspace it needs (the same
 // plan serves pkv_decode_workspace_bytes and the call).
@@ -69,6 +77,9 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t max_ctx, int32_t Hq, int32_t Hk
                        int32_t bs, int dtype, int32_t partition_size);
 // Returns hipErrorNotSupported when no kernel covers the shape/dtype.
 hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &plan, int dtype, hipStream_t stream);
+// Whether launch_decode runs the fixed-partition kernel that can take the
+// store (a.st_k set) into its own launch.
+bool decode_store_fusable(const DecodeArgs &a, const DecodePlan &plan, int dtype);
 
 struct PrefillArgs {
     const void *q;

@@ -19,7 +19,8 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-from . import decode_attention_paged, decode_workspace_bytes, store_kvcache
+from . import (decode_attention_paged, decode_store_attention_paged, decode_workspace_bytes,
+               store_kvcache)
 
 BUCKETS: List[int] = [1, 2, 4, 8] + list(range(16, 513, 16))
 
@@ -39,12 +40,18 @@ class DecodeGraphs:
     ``run`` takes one step's inputs -- per layer q [B, Hq, d] and the new
     token's k, v [B, Hkv, d], plus the shared slot_mapping [B], context_lens
     [B] and block_tables [B, w] (int32, device) -- and returns the per-layer
-    outputs (views of static buffers, valid until the next run)."""
+    outputs (views of static buffers, valid until the next run).
+
+    With ``fuse_store`` (the default) each layer is one
+    decode_store_attention_paged call, which on the fixed-partition path of
+    small batches runs the store inside the attention launch; without it, a
+    store_kvcache call and a decode_attention_paged call."""
 
     def __init__(self, layers: Sequence[Tuple[torch.Tensor, torch.Tensor]], num_q_heads: int,
                  max_context_len: int, max_blocks_per_seq: int, scale: float,
-                 buckets: Sequence[int] = BUCKETS):
+                 buckets: Sequence[int] = BUCKETS, fuse_store: bool = True):
         self.layers = list(layers)
+        self.fuse_store = bool(fuse_store)
         kc = self.layers[0][0]
         _, bs, hkv, d = kc.shape
         self.dtype, self.device = kc.dtype, kc.device
@@ -69,6 +76,12 @@ class DecodeGraphs:
 
     def _step(self, b: int) -> None:
         for l, (kc, vc) in enumerate(self.layers):
+            if self.fuse_store:
+                decode_store_attention_paged(self.q[l, :b], self.k[l, :b], self.v[l, :b], kc, vc,
+                                             self.slots[:b], self.tables[:b], self.ctx[:b],
+                                             self.max_ctx, self.scale, out=self.out[l, :b],
+                                             workspace=self.workspace)
+                continue
             store_kvcache(self.k[l, :b], self.v[l, :b], kc, vc, self.slots[:b])
             decode_attention_paged(self.q[l, :b], kc, vc, self.tables[:b], self.ctx[:b],
                                    self.max_ctx, self.scale, out=self.out[l, :b],
@@ -137,6 +150,11 @@ class DecodeGraphs:
         outs = []
         mc = self.max_ctx if max_context_len is None else int(max_context_len)
         for l, (kc, vc) in enumerate(self.layers):
+            if self.fuse_store:
+                outs.append(decode_store_attention_paged(q[l], k[l], v[l], kc, vc, slot_mapping,
+                                                         block_tables, context_lens, mc, self.scale,
+                                                         workspace=self.workspace))
+                continue
             store_kvcache(k[l], v[l], kc, vc, slot_mapping)
             outs.append(decode_attention_paged(q[l], kc, vc, block_tables, context_lens, mc,
                                                self.scale, workspace=self.workspace))
