@@ -12,8 +12,9 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (decode_attention_paged, decode_workspace_bytes, pack_decode, pack_prefill,
-               prefill_attention_varlen, prefill_store_attention_varlen, store_kvcache)
+from . import (decode_attention_paged, decode_store_attention_paged, decode_workspace_bytes,
+               pack_decode, pack_prefill, prefill_attention_varlen, prefill_store_attention_varlen,
+               store_kvcache)
 
 
 def alloc_pool(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
@@ -63,6 +64,12 @@ def run_step(s: StepInputs, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
     dev = k_cache.device
     if s.phase == "decode":
         meta = pack_decode(s.seq_lens, s.block_tables, s.block_size, device=dev, stream=stream)
+        if s.fuse_store:
+            return decode_store_attention_paged(q, k_new, v_new, k_cache, v_cache, meta["slot_mapping"],
+                                                meta["block_tables"], meta["context_lens"],
+                                                meta["max_seqlen_k"], s.scale, out=out,
+                                                partition_size=s.partition_size, workspace=workspace,
+                                                stream=stream)
         store_kvcache(k_new, v_new, k_cache, v_cache, meta["slot_mapping"], stream=stream)
         return decode_attention_paged(q, k_cache, v_cache, meta["block_tables"],
                                       meta["context_lens"], meta["max_seqlen_k"], s.scale,

@@ -120,3 +120,21 @@ def test_fused_decode_rejects_disagreeing_tensors(cuda):
         pkv.decode_store_attention_paged(q, kv.float(), kv, kc, vc, slots, bt, ctx, 1, 0.1)
     with pytest.raises(ValueError):      # slot_mapping shorter than the batch
         pkv.decode_store_attention_paged(q, kv, kv, kc, vc, slots[:1], bt, ctx, 1, 0.1)
+
+
+def test_run_step_with_fused_store_equals_two_calls(cuda):
+    say("[gpu] run_step(fuse_store=True) on a small decode batch against the two-call step")
+    from paged_kv_cache_125_amd.step import run_step, step_inputs_of
+    w = custom_workload(phase="decode", seq_lens=[700, 1300, 64, 2049], num_cached=[699, 1299, 63, 2048],
+                        num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=256, seed=11)
+    wd = to_device(w, "cuda")
+    pools = []
+    outs = []
+    for fuse in (False, True):
+        kc, vc = alloc_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype, "cuda")
+        write_ranges(w.hist, w.block_tables, w.block_size, wd.k_hist, wd.v_hist, kc, vc)
+        outs.append(run_step(step_inputs_of(w, fuse_store=fuse), wd.q, wd.k_new, wd.v_new, kc, vc))
+        pools.append((kc, vc))
+    torch.cuda.synchronize()
+    assert np.array_equal(raw(outs[0]), raw(outs[1]))
+    assert np.array_equal(raw(pools[0][0]), raw(pools[1][0])) and np.array_equal(raw(pools[0][1]), raw(pools[1][1]))
